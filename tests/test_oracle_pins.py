@@ -1,0 +1,431 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Brute force on tiny inputs (pure-Python loops with math.fsum), closed forms,
+invariants of the mathematics, exhaustive subset search for the selection
+rule, the worked counting example the WISE pull request page prints, and
+the fallback transitions it names.  The last test plants mistakes in the
+oracle and checks that these pins catch them.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import wise_oracle as O
+from block_sparse_paged_split_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def brute_softmax_attention(q, K, V, scale):
+    """Textbook softmax attention with Python floats and math.fsum."""
+    n, d = len(K), len(q)
+    s = [scale * math.fsum(q[i] * K[t][i] for i in range(d)) for t in range(n)]
+    mx = max(s)
+    w = [math.exp(x - mx) for x in s]
+    Z = math.fsum(w)
+    o = [math.fsum(w[t] * V[t][j] for t in range(n)) / Z for j in range(len(V[0]))]
+    return o, [wt / Z for wt in w]
+
+
+def rand_qkv(rng, n, d):
+    return rng.standard_normal(d), rng.standard_normal((n, d)), rng.standard_normal((n, d))
+
+
+def paged_case(rng, n, d=8, H=2, P=16, shuffle=True, spare=2):
+    """A tiny paged layout (fp32 encoded) with a known logical K/V per head."""
+    npg = (n + P - 1) // P
+    num_pages = npg + spare
+    phys = rng.permutation(num_pages)[:npg] if shuffle else np.arange(npg)
+    Kl = rng.standard_normal((H, n, d)).astype(np.float32)
+    Vl = rng.standard_normal((H, n, d)).astype(np.float32)
+    k = np.full((num_pages, H, P, d), np.nan, np.float32)
+    v = np.full((num_pages, H, P, d), np.nan, np.float32)
+    for j in range(npg):
+        lo, hi = j * P, min(n, j * P + P)
+        k[phys[j], :, : hi - lo] = Kl[:, lo:hi]
+        v[phys[j], :, : hi - lo] = Vl[:, lo:hi]
+    bt = np.full((1, npg + 1), -1, np.int32)
+    bt[0, :npg] = phys
+    q = rng.standard_normal((1, H, d)).astype(np.float32)
+    return dict(q=q, k_cache=k, v_cache=v, block_table=bt, ctx_len=np.array([n], np.int32),
+                page_size=P, num_pages=num_pages, max_ctx=(npg + 1) * P), Kl, Vl
+
+
+def state(slots=1, layers=1, heads=2, words=1):
+    return (np.zeros((slots, layers, heads, words), np.uint32),
+            np.zeros((slots, layers), O.TAG_DTYPE))
+
+
+# ----------------------------------------------------------------------------- O2 dense
+
+@pytest.mark.parametrize("n,d", [(1, 4), (7, 3), (33, 8), (64, 5)])
+def test_dense_matches_brute_force(n, d):
+    rng = np.random.default_rng(n * 100 + d)
+    q, K, V = rand_qkv(rng, n, d)
+    scale = 0.7
+    ref, _ = brute_softmax_attention(q.tolist(), K.tolist(), V.tolist(), scale)
+    got = O.dense_attention(q, K, V, scale)
+    np.testing.assert_allclose(got["o"], ref, rtol=0, atol=1e-12)
+    # (M, L) are the max and the normaliser of exp(s - M)
+    s = scale * (K @ q)
+    assert got["M"] == pytest.approx(max(s), abs=1e-12)
+    assert got["L"] == pytest.approx(math.fsum(math.exp(x - max(s)) for x in s), rel=1e-13)
+
+
+def test_dense_closed_forms():
+    rng = np.random.default_rng(1)
+    d, n = 6, 40
+    q = rng.standard_normal(d)
+    V = rng.standard_normal((n, d))
+    K = np.tile(rng.standard_normal(d), (n, 1))            # all keys equal
+    np.testing.assert_allclose(O.dense_attention(q, K, V, 1.0)["o"], V.mean(0), atol=1e-14)
+    K = rng.standard_normal((n, d)) * 1e-3                   # one key +60 logits above the rest
+    K[17] = q * (60.0 / (q @ q))
+    np.testing.assert_allclose(O.dense_attention(q, K, V, 1.0)["o"], V[17], atol=1e-20)
+
+
+def test_default_scale():
+    assert O.default_scale(64) == 0.125
+    assert O.default_scale(128) == pytest.approx(1 / math.sqrt(128), rel=1e-16)
+
+
+# ----------------------------------------------------------------------------- O3/O4 tile stats
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 95, 200])
+def test_tile_stats_and_mass(n):
+    rng = np.random.default_rng(n)
+    q, K, V = rand_qkv(rng, n, 4)
+    att = O.dense_attention(q, K, V, 0.9)
+    m, l = O.tile_stats(att["s"])
+    nb = (n + 31) // 32
+    assert len(m) == nb
+    # recombining the tiles reproduces the row's (M, L)
+    M = m.max()
+    assert M == att["M"]
+    assert float(np.sum(l * np.exp(m - M))) == pytest.approx(att["L"], rel=1e-13)
+    # masses are the brute-force block sums of the full softmax and sum to one
+    _, probs = brute_softmax_attention(q.tolist(), K.tolist(), V.tolist(), 0.9)
+    p = O.block_mass(m, l, att["M"], att["L"])
+    brute = [math.fsum(probs[32 * b: min(n, 32 * b + 32)]) for b in range(nb)]
+    np.testing.assert_allclose(p, brute, rtol=0, atol=1e-14)
+    assert float(p.sum()) == pytest.approx(1.0, abs=1e-13)
+    # per-tile definition, brute force
+    for b in range(nb):
+        seg = att["s"][32 * b: min(n, 32 * b + 32)]
+        assert m[b] == max(seg)
+        assert l[b] == pytest.approx(math.fsum(math.exp(x - max(seg)) for x in seg), rel=1e-14)
+
+
+# ----------------------------------------------------------------------------- O5 selection
+
+def brute_select(p, eta):
+    """Smallest cardinality subset with mass >= eta; among those, the heaviest."""
+    nb = len(p)
+    for k in range(1, nb + 1):
+        best = None
+        for c in itertools.combinations(range(nb), k):
+            mass = math.fsum(p[i] for i in c)
+            if mass >= eta and (best is None or mass > best[0]):
+                best = (mass, c)
+        if best is not None:
+            return k, sorted(best[1])
+    return nb, list(range(nb))
+
+
+@pytest.mark.parametrize("nb", [1, 2, 5, 9, 12])
+@pytest.mark.parametrize("eta", [0.5, 0.9, 0.95, 0.99])
+def test_selection_brute_force(nb, eta):
+    rng = np.random.default_rng(nb * 7 + int(eta * 100))
+    for _ in range(3):
+        w = rng.exponential(size=nb) ** 3
+        p = w / w.sum()
+        k, blocks = brute_select(p.tolist(), eta)
+        sel = O.eta_select(p, eta)
+        assert sel.K == k
+        assert sel.blocks.tolist() == blocks
+        assert sel.c_prev < eta <= sel.c_K or (sel.K == nb and sel.c_K < eta)
+
+
+def test_selection_tie_break_equal_masses():
+    # identical keys: every full 32-token block has the same mass; the order
+    # among equals is by block index, so the support is blocks 0..ceil(eta*nb)-1
+    nb, d = 30, 4
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal(d)
+    K = np.tile(rng.standard_normal(d), (32 * nb, 1))
+    att = O.dense_attention(q, K, K, 1.0)
+    p = O.block_mass(*O.tile_stats(att["s"]), att["M"], att["L"])
+    for eta in (0.91, 0.95, 0.47):               # eta * nb is not an integer
+        sel = O.eta_select(p, eta)
+        assert sel.blocks.tolist() == list(range(math.ceil(eta * nb)))
+
+
+def test_selection_dominant_and_single_block():
+    p = np.full(10, 0.004)
+    p[6] = 1 - 0.036
+    assert O.eta_select(p, 0.95).blocks.tolist() == [6]
+    assert O.eta_select(np.array([1.0]), 0.95).blocks.tolist() == [0]     # n <= 32
+    assert O.eta_select(np.array([1.0]), 1.0).K == 1
+    # equality reaches eta
+    assert O.eta_select(np.array([0.5, 0.25, 0.25]), 0.75).blocks.tolist() == [0, 1]
+
+
+def test_selection_nesting():
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        w = rng.standard_normal(64) * 2
+        p = np.exp(w) / np.exp(w).sum()
+        s90, s95, s99 = (set(O.eta_select(p, e).blocks.tolist()) for e in (0.9, 0.95, 0.99))
+        assert s90 <= s95 <= s99
+
+
+def test_bitmask_roundtrip():
+    blocks = [0, 1, 31, 32, 63, 100]
+    bits = O.blocks_to_bits(blocks, 4)
+    assert bits[0] == (1 | 2 | (1 << 31)) and bits[1] == (1 | (1 << 31)) and bits[3] == (1 << 4)
+    assert O.bits_to_blocks(bits, 128).tolist() == blocks
+    assert O.bits_to_blocks(bits, 64).tolist() == [0, 1, 31, 32, 63]
+
+
+# ----------------------------------------------------------------------------- O7 masked
+
+def test_masked_attention():
+    rng = np.random.default_rng(5)
+    n, d = 100, 5
+    q, K, V = rand_qkv(rng, n, d)
+    np.testing.assert_allclose(O.masked_attention(q, K, V, 0.5, range(4)),
+                               O.dense_attention(q, K, V, 0.5)["o"], atol=1e-15)
+    ref, _ = brute_softmax_attention(q.tolist(), K[64:96].tolist(), V[64:96].tolist(), 0.5)
+    np.testing.assert_allclose(O.masked_attention(q, K, V, 0.5, [2]), ref, atol=1e-12)
+    ref, _ = brute_softmax_attention(q.tolist(), K[96:].tolist(), V[96:].tolist(), 0.5)
+    np.testing.assert_allclose(O.masked_attention(q, K, V, 0.5, [3]), ref, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- whole call
+
+def test_call_dense_discover_sparse_and_page_permutation():
+    rng = np.random.default_rng(11)
+    case, Kl, Vl = paged_case(rng, 150, H=2)
+    sup, tags = state(heads=2)
+    common = dict(layer=0, row_request=[7], row_position=[42], required=1, eta=0.9)
+    d = O.run_call(**case, modes=[O.DENSE])
+    for h in range(2):
+        np.testing.assert_allclose(
+            d.out[0, h], O.dense_attention(case["q"][0, h].astype(float), Kl[h].astype(float),
+                                           Vl[h].astype(float), 1 / math.sqrt(8))["o"], atol=1e-14)
+    c = O.run_call(**case, modes=[O.DISCOVER], support=sup, tags=tags, **common)
+    assert np.array_equal(c.out, d.out)                      # discover output is the dense output
+    assert c.tags[0, 0]["discoveries"] == 1 and c.tags[0, 0]["position"] == 42
+    s = O.run_call(**case, modes=[O.SPARSE], support=c.support, tags=c.tags, **common)
+    assert s.counters[0] == 0
+    for h in range(2):
+        blocks = c.units[(0, h)].selection.blocks
+        assert O.bits_to_blocks(c.support[0, 0, h], 5).tolist() == blocks.tolist()
+        ref = O.masked_attention(case["q"][0, h].astype(float), Kl[h].astype(float),
+                                 Vl[h].astype(float), 1 / math.sqrt(8), blocks)
+        np.testing.assert_allclose(s.out[0, h], ref, atol=1e-14)
+    # all blocks selected: sparse equals dense
+    full = c.support.copy()
+    full[...] = 0x1F
+    s_all = O.run_call(**case, modes=[O.SPARSE], support=full, tags=c.tags, **common)
+    np.testing.assert_allclose(s_all.out, d.out, atol=1e-14)
+    # a different physical page order gives the same results
+    perm = rng.permutation(case["num_pages"])
+    inv = np.argsort(perm)
+    case2 = dict(case)
+    case2["k_cache"] = case["k_cache"][inv]
+    case2["v_cache"] = case["v_cache"][inv]
+    bt = case["block_table"].copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    case2["block_table"] = bt
+    c2 = O.run_call(**case2, modes=[O.DISCOVER], support=sup, tags=tags, **common)
+    np.testing.assert_allclose(c2.out, c.out, atol=1e-14)
+    assert np.array_equal(c2.support, c.support)
+
+
+def _two_block_row(rng, hot_block, d=8):
+    """n = 64 (two causal blocks) where one block holds nearly all the mass."""
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    K = rng.standard_normal((1, 64, d)).astype(np.float32) * 0.01
+    K[0, 32 * hot_block: 32 * hot_block + 32, 0] = 40.0
+    k = K.reshape(1, 2, 32, d).transpose(1, 0, 2, 3).copy()
+    v = rng.standard_normal(k.shape).astype(np.float32)
+    return dict(q=q, k_cache=k, v_cache=v, block_table=np.array([[0, 1]], np.int32),
+                ctx_len=np.array([64], np.int32), page_size=32, num_pages=2, max_ctx=64)
+
+
+def test_union_density_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "union_density_example.json")))
+    rng = np.random.default_rng(2)
+    sup, tags = state(heads=1)
+    common = dict(layer=0, row_request=[1], row_position=[5], required=2, eta=0.9)
+    c0 = O.run_call(**_two_block_row(rng, 0), modes=[O.DISCOVER], support=sup, tags=tags, **common)
+    assert c0.units[(0, 0)].selection.blocks.tolist() == g["depth0_selection"]
+    c1 = O.run_call(**_two_block_row(rng, 1), modes=[O.DISCOVER_UNION], support=c0.support,
+                    tags=c0.tags, **common)
+    assert c1.units[(0, 0)].selection.blocks.tolist() == g["depth1_selection"]
+    total = c0.counters + c1.counters
+    assert total[2] == g["causal_blocks"]
+    assert O.density(total) == g["expected_union_density"]
+    indiv = (c0.units[(0, 0)].selection.K + c1.units[(0, 0)].selection.K) / (2 * g["causal_blocks"])
+    assert indiv == g["density_of_individual_selections"]
+    assert O.bits_to_blocks(c1.support[0, 0, 0], 2).tolist() == [0, 1]
+    assert c1.tags[0, 0]["discoveries"] == 2
+    # the reuse depth attends the union: with every block in it, sparse equals dense
+    case = _two_block_row(rng, 1)
+    s = O.run_call(**case, modes=[O.SPARSE], support=c1.support, tags=c1.tags, **common)
+    d = O.run_call(**case, modes=[O.DENSE])
+    assert s.counters[0] == 0
+    np.testing.assert_allclose(s.out, d.out, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- O8 fallback
+
+def _discovered(rng, required=2):
+    case, _, _ = paged_case(rng, 96, H=2)
+    sup, tags = state(heads=2)
+    common = dict(layer=0, row_request=[3], row_position=[10], required=required, eta=0.95)
+    c0 = O.run_call(**case, modes=[O.DISCOVER], support=sup, tags=tags, **common)
+    return case, common, c0
+
+
+def test_fallback_transitions():
+    rng = np.random.default_rng(4)
+    case, common, c0 = _discovered(rng)
+    dense = O.run_call(**case, modes=[O.DENSE]).out
+    # complete window: union then sparse, no fallback
+    c1 = O.run_call(**case, modes=[O.DISCOVER_UNION], support=c0.support, tags=c0.tags, **common)
+    ok = O.run_call(**case, modes=[O.SPARSE], support=c1.support, tags=c1.tags, **common)
+    assert c1.counters[0] == 0 and ok.counters[0] == 0 and ok.effective[0] == O.SPARSE
+    # incomplete window: one discovery of the two required -> dense, counted
+    r = O.run_call(**case, modes=[O.SPARSE], support=c0.support, tags=c0.tags, **common)
+    assert r.counters[0] == 1 and r.effective[0] == O.DENSE
+    assert np.array_equal(r.out, dense)
+    # stale position: the tag belongs to the previous token
+    stale = dict(common, row_position=[11])
+    r = O.run_call(**case, modes=[O.SPARSE], support=c1.support, tags=c1.tags, **stale)
+    assert r.counters[0] == 1 and np.array_equal(r.out, dense)
+    # released slot: discoveries cleared by the owner
+    rel = c1.tags.copy()
+    rel[0, 0]["discoveries"] = 0
+    r = O.run_call(**case, modes=[O.SPARSE], support=c1.support, tags=rel, **common)
+    assert r.counters[0] == 1 and np.array_equal(r.out, dense)
+    # another request's support in this slot
+    other = dict(common, row_request=[4])
+    r = O.run_call(**case, modes=[O.SPARSE], support=c1.support, tags=c1.tags, **other)
+    assert r.counters[0] == 1
+    # broken window: the union depth sees no discovery for this position; it
+    # runs dense, invalidates the tag, and the reuse depths fall back too
+    b = O.run_call(**case, modes=[O.DISCOVER_UNION], support=c0.support, tags=c0.tags, **stale)
+    assert b.counters[0] == 1 and np.array_equal(b.out, dense)
+    assert b.tags[0, 0]["discoveries"] == 0
+    assert np.array_equal(b.support, c0.support)             # nothing recorded
+    r = O.run_call(**case, modes=[O.SPARSE], support=b.support, tags=b.tags, **stale)
+    assert r.counters[0] == 1
+    # a dense row never touches the state
+    r = O.run_call(**case, modes=[O.DENSE], support=c1.support, tags=c1.tags, **common)
+    assert r.counters.tolist() == [0, 0, 0, 0] and np.array_equal(r.tags, c1.tags)
+
+
+def test_data_errors():
+    rng = np.random.default_rng(6)
+    case, common, c0 = _discovered(rng, required=1)
+    bad = dict(case, ctx_len=np.array([case["max_ctx"] + 1], np.int32))
+    r = O.run_call(**bad, modes=[O.DENSE])
+    assert np.isnan(r.out).all() and r.counters[3] == 2
+    bad = dict(case, ctx_len=np.array([0], np.int32))
+    assert O.run_call(**bad, modes=[O.DENSE]).counters[3] == 2
+    # a bad page id inside the attended range
+    bt = case["block_table"].copy()
+    bt[0, 1] = case["num_pages"]
+    r = O.run_call(**dict(case, block_table=bt), modes=[O.DENSE])
+    assert np.isnan(r.out).all() and r.counters[3] == 2
+    # outside every head's support it is harmless for a sparse row
+    sup = c0.support.copy()
+    sup[...] = 0b001                                          # block 0 only (tokens 0..31, page 0..1)
+    bt = case["block_table"].copy()
+    bt[0, 5] = -7                                             # tokens 80..95 -> block 2
+    r = O.run_call(**dict(case, block_table=bt), modes=[O.SPARSE], support=sup, tags=c0.tags, **common)
+    assert r.counters[3] == 0 and not np.isnan(r.out).any()
+    # an empty support
+    sup[0, 0, 1] = 0
+    r = O.run_call(**case, modes=[O.SPARSE], support=sup, tags=c0.tags, **common)
+    assert r.counters[3] == 1 and np.isnan(r.out[0, 1]).all() and not np.isnan(r.out[0, 0]).any()
+    # slot out of range for a stateful row; invalid mode
+    r = O.run_call(**case, modes=[O.SPARSE], support=sup, tags=c0.tags, slot_of_row=[5], **common)
+    assert r.counters[3] == 2
+    r = O.run_call(**case, modes=[9], support=sup, tags=c0.tags, **common)
+    assert r.counters[3] == 2
+
+
+# ----------------------------------------------------------------------------- generator sanity
+
+def test_synth_encodings_and_layout():
+    x = np.array([1.0, -2.5, 3.140625, 1.00390625, 1.01171875, 65504.0], np.float32)
+    b = synth.f32_to_bf16_bits(x)
+    # 1.00390625 = 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa wins (1.0)
+    # 1.01171875 = 1 + 3*2^-8 ties between 1+2^-7 and 1+2^-6: even is 1+2^-6
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(b),
+                                  np.array([1.0, -2.5, 3.140625, 1.0, 1.015625, 65536.0], np.float32))
+    w = synth.WORKLOADS["tiny_f32"]
+    li = synth.layer_inputs(w, depth=0)
+    assert li.k.shape == (8 + w.spare_pages, 4, 32, 64)
+    assert li.block_table[0].tolist() == list(range(8))
+    q, K, V = synth.row_qkv(w, 0, 0, 0, 256)
+    np.testing.assert_array_equal(li.k[3, 2, 5], K[2, 3 * 32 + 5])
+    w = synth.WORKLOADS["ctx1k"]
+    li = synth.layer_inputs(w, depth=1, rows=[3])
+    q, K, V = synth.row_qkv(w, 1, 0, 3, 1024)
+    page = li.block_table[3, 10]
+    np.testing.assert_array_equal(li.k[page, 7, 4], synth.f32_to_bf16_bits(K[7, 164]))
+    assert len(set(li.block_table[li.block_table >= 0].tolist())) == (li.block_table >= 0).sum()
+    ctx = synth.context_lengths(synth.WORKLOADS["ragged"])
+    assert ctx.min() >= 512 and ctx.max() <= 32768
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Each plausible slip in the oracle makes at least one pin above fail."""
+    real_select, real_mass, real_stats = O.eta_select, O.block_mass, O.tile_stats
+
+    def strict_cut(p, eta):                     # '>' instead of '>=' at the cut
+        sel = real_select(p, eta)
+        c = np.cumsum(np.asarray(p)[sel.order])
+        K = int(np.nonzero(c > eta)[0][0]) + 1 if np.any(c > eta) else len(p)
+        return O.Selection(sel.order, K, np.sort(sel.order[:K]), 0, c[K - 1], 0, 0)
+
+    def index_desc(p, eta):                     # ties broken by descending index
+        p = np.asarray(p)
+        order = np.lexsort((-np.arange(len(p)), -p))
+        c = np.cumsum(p[order])
+        K = int(np.nonzero(c >= eta)[0][0]) + 1
+        return O.Selection(order, K, np.sort(order[:K]), 0, c[K - 1], 0, 0)
+
+    def no_norm(m, l, M, L):                    # forgot to divide by L
+        return l * np.exp(m - M)
+
+    def last_tile_full(s):                      # tile stats over a padded last tile
+        m, l = real_stats(np.concatenate([s, np.zeros((-len(s)) % 32)]))
+        return m, l
+
+    planted = [
+        ("eta_select", strict_cut, lambda: test_selection_dominant_and_single_block()),
+        ("eta_select", index_desc, lambda: test_selection_tie_break_equal_masses()),
+        ("block_mass", no_norm, lambda: test_tile_stats_and_mass(95)),
+        ("tile_stats", last_tile_full, lambda: test_tile_stats_and_mass(33)),
+    ]
+    for name, fn, pin in planted:
+        monkeypatch.setattr(O, name, fn)
+        with pytest.raises(AssertionError):
+            pin()
+        monkeypatch.setattr(O, name, {"eta_select": real_select, "block_mass": real_mass,
+                                      "tile_stats": real_stats}[name])
