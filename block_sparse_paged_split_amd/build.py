@@ -1,0 +1,48 @@
+"""Build libwise.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: python -m block_sparse_paged_split_amd.build
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SOURCES = ["wise_api.hip", "wise_split.hip", "wise_finish.hip"]
+LIB = os.path.join(PKG, "libwise.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: ROCm is required to build libwise")
+
+
+def command(out: str = LIB, extra=()):
+    src = [os.path.join(PKG, "csrc", s) for s in SOURCES]
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            # packed fp32 instructions are kept out of the generated code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+            *extra, *src, "-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("libwise build failed")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,257 @@
+// Host entry points of libwise: argument validation, workspace layout, and
+// the launches of the split-KV kernel and the finish kernel on the caller's
+// stream.  Nothing is allocated, nothing is synchronised.
+#include <cmath>
+#include <cstdint>
+
+#include "wise_internal.h"
+
+namespace wise {
+
+int tiles_per_item(int max_blocks) {
+  (void)max_blocks;
+  return 8;  // ~eight tiles per program, as the split design prescribes
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool make_layout(int rows, int heads, int head_dim, int max_ctx, Layout *L) {
+  if (rows < 1 || heads < 1 || (head_dim != 64 && head_dim != 128)) return false;
+  if (max_ctx < 1 || max_ctx > kMaxCtx) return false;
+  if (static_cast<int64_t>(rows) * heads > (int64_t{1} << 22)) return false;
+  L->rows = rows;
+  L->heads = heads;
+  L->head_dim = head_dim;
+  L->max_ctx = max_ctx;
+  L->max_blocks = (max_ctx + kBlock - 1) / kBlock;
+  L->tiles_per_item = tiles_per_item(L->max_blocks);
+  L->items_per_unit = (L->max_blocks + L->tiles_per_item - 1) / L->tiles_per_item;
+  if (L->items_per_unit > kMaxItemsPerUnit || L->tiles_per_item > kMaxTilesPerItem) return false;
+  const size_t units = static_cast<size_t>(rows) * heads;
+  const size_t slots = units * L->items_per_unit;
+  size_t off = 0;
+  L->off_row_code = off;
+  off += align256(sizeof(int32_t) * rows);
+  L->off_unit_items = off;
+  off += align256(sizeof(int32_t) * units);
+  L->off_part_ml = off;
+  off += align256(sizeof(float2) * slots);
+  L->off_part_acc = off;
+  off += align256(sizeof(float) * slots * head_dim);
+  L->off_stats = off;
+  off += align256(sizeof(float2) * units * L->max_blocks);
+  L->total = off;
+  // the split grid (units x item groups) must fit one launch dimension
+  const int64_t groups = (L->items_per_unit + kWavesPerGroup - 1) / kWavesPerGroup;
+  if (static_cast<int64_t>(units) * groups > INT32_MAX) return false;
+  return true;
+}
+
+}  // namespace wise
+
+using namespace wise;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+wise_status check_attn(const wise_attn *a, Layout *L) {
+  if (!a) return WISE_E_ARG;
+  if (a->dtype != WISE_BF16 && a->dtype != WISE_F32) return WISE_E_UNSUPPORTED;
+  if (a->head_dim != 64 && a->head_dim != 128) return WISE_E_UNSUPPORTED;
+  if (a->rows < 1 || a->heads < 1 || a->max_ctx < 1 || a->num_pages < 1) return WISE_E_ARG;
+  if (!is_pow2(a->page_size) || a->page_size < 8 || a->page_size > 4096) return WISE_E_UNSUPPORTED;
+  if (a->max_ctx > kMaxCtx) return WISE_E_UNSUPPORTED;
+  if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->ctx_len || !a->out) return WISE_E_ARG;
+  if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->out, 16))
+    return WISE_E_ARG;
+  if (a->tile_stats && !aligned(a->tile_stats, 8)) return WISE_E_ARG;
+  const int64_t e = a->dtype == WISE_BF16 ? 2 : 4;
+  if (a->stride_page <= 0 || a->stride_head <= 0 || a->stride_token <= 0) return WISE_E_ARG;
+  if ((a->stride_page * e) % 16 || (a->stride_head * e) % 16 || (a->stride_token * e) % 16) return WISE_E_ARG;
+  if (a->stride_token * e * 8 > INT32_MAX / 2) return WISE_E_UNSUPPORTED;
+  if (a->stride_token < a->head_dim) return WISE_E_ARG;
+  const int64_t need_bt = (static_cast<int64_t>(a->max_ctx) + a->page_size - 1) / a->page_size;
+  if (a->bt_stride < need_bt) return WISE_E_ARG;
+  if (!std::isfinite(a->scale) || a->scale < 0.0f) return WISE_E_ARG;
+  if ((a->ev_split_begin == nullptr) != (a->ev_split_end == nullptr)) return WISE_E_ARG;
+  if (!make_layout(a->rows, a->heads, a->head_dim, a->max_ctx, L)) return WISE_E_UNSUPPORTED;
+  return WISE_OK;
+}
+
+wise_status check_support(const wise_attn *a, const wise_support *s, const Layout &L) {
+  if (!s) return WISE_E_ARG;
+  if (!s->support || !s->tags || !s->row_request || !s->row_position) return WISE_E_ARG;
+  if (s->slots < 1 || s->layers < 1 || s->layer < 0 || s->layer >= s->layers) return WISE_E_ARG;
+  if (s->words < (L.max_blocks + 31) / 32) return WISE_E_ARG;
+  if (s->discoveries_required < 1) return WISE_E_ARG;
+  if (!(s->eta > 0.0f && s->eta <= 1.0f)) return WISE_E_ARG;
+  if (!aligned(s->support, 4) || !aligned(s->tags, 8) || (s->counters && !aligned(s->counters, 8)))
+    return WISE_E_ARG;
+  (void)a;
+  return WISE_OK;
+}
+
+wise_status check_ws(void *ws, size_t ws_bytes, const Layout &L) {
+  if (!ws || !aligned(ws, 256)) return WISE_E_WORKSPACE;
+  if (ws_bytes < L.total) return WISE_E_WORKSPACE;
+  return WISE_OK;
+}
+
+float qk_scale_log2(const wise_attn *a) {
+  const double sc = a->scale > 0.0f ? static_cast<double>(a->scale) : 1.0 / std::sqrt(static_cast<double>(a->head_dim));
+  return static_cast<float>(sc * 1.4426950408889634074);  // log2(e)
+}
+
+int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, const uint8_t *row_mode,
+                   void *ws, size_t ws_bytes, void *stream) {
+  Layout L;
+  wise_status st = check_attn(a, &L);
+  if (st != WISE_OK) return st;
+  const bool stateful = uniform_mode != WISE_DENSE || row_mode != nullptr;
+  if (stateful) {
+    st = check_support(a, s, L);
+    if (st != WISE_OK) return st;
+  }
+  st = check_ws(ws, ws_bytes, L);
+  if (st != WISE_OK) return st;
+
+  const int64_t e = a->dtype == WISE_BF16 ? 2 : 4;
+  char *w = static_cast<char *>(ws);
+  SplitParams p{};
+  p.q = a->q;
+  p.k = a->k_cache;
+  p.v = a->v_cache;
+  p.stride_page_b = a->stride_page * e;
+  p.stride_head_b = a->stride_head * e;
+  p.stride_token_b = a->stride_token * e;
+  p.block_table = a->block_table;
+  p.bt_stride = a->bt_stride;
+  p.ctx_len = a->ctx_len;
+  p.rows = a->rows;
+  p.heads = a->heads;
+  p.max_ctx = a->max_ctx;
+  p.max_blocks = L.max_blocks;
+  p.num_pages = a->num_pages;
+  p.page_shift = log2i(a->page_size);
+  p.qk_scale_log2 = qk_scale_log2(a);
+  p.tiles_per_item = L.tiles_per_item;
+  p.items_per_unit = L.items_per_unit;
+  p.chunk_groups = (L.items_per_unit + kWavesPerGroup - 1) / kWavesPerGroup;
+  p.row_mode = row_mode;
+  p.uniform_mode = uniform_mode;
+  if (stateful) {
+    p.support = s->support;
+    p.slots = s->slots;
+    p.layers = s->layers;
+    p.layer = s->layer;
+    p.words = s->words;
+    p.required = s->discoveries_required;
+    p.slot_of_row = s->slot_of_row;
+    p.tags = s->tags;
+    p.row_request = s->row_request;
+    p.row_position = s->row_position;
+    p.counters = reinterpret_cast<unsigned long long *>(s->counters);
+  }
+  p.row_code = reinterpret_cast<int32_t *>(w + L.off_row_code);
+  p.unit_items = reinterpret_cast<int32_t *>(w + L.off_unit_items);
+  p.part_ml = reinterpret_cast<float2 *>(w + L.off_part_ml);
+  p.part_acc = reinterpret_cast<float *>(w + L.off_part_acc);
+  p.stats = reinterpret_cast<float2 *>(w + L.off_stats);
+  p.stats_export = reinterpret_cast<float2 *>(a->tile_stats);
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (a->ev_split_begin && hipEventRecord(static_cast<hipEvent_t>(a->ev_split_begin), strm) != hipSuccess)
+    return WISE_E_HIP;
+  if (launch_split(p, a->dtype, a->head_dim, strm) != hipSuccess) return WISE_E_HIP;
+  if (a->ev_split_end && hipEventRecord(static_cast<hipEvent_t>(a->ev_split_end), strm) != hipSuccess)
+    return WISE_E_HIP;
+  return WISE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wise_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t max_ctx) {
+  Layout L;
+  return make_layout(rows, heads, head_dim, max_ctx, &L) ? L.total : 0;
+}
+
+wise_status wise_decode_dense(const wise_attn *a, void *ws, size_t ws_bytes, void *stream) {
+  return decode(a, nullptr, WISE_DENSE, nullptr, ws, ws_bytes, stream);
+}
+
+wise_status wise_decode_discover(const wise_attn *a, const wise_support *s, int32_t union_with_previous,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  return decode(a, s, union_with_previous ? WISE_DISCOVER_UNION : WISE_DISCOVER, nullptr, ws, ws_bytes,
+                stream);
+}
+
+wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s, const uint8_t *row_mode, void *ws,
+                               size_t ws_bytes, void *stream) {
+  return decode(a, s, WISE_SPARSE, row_mode, ws, ws_bytes, stream);
+}
+
+wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws, size_t ws_bytes,
+                               void *stream) {
+  Layout L;
+  wise_status st = check_attn(a, &L);
+  if (st != WISE_OK) return st;
+  if (s) {
+    st = check_support(a, s, L);
+    if (st != WISE_OK) return st;
+  }
+  st = check_ws(ws, ws_bytes, L);
+  if (st != WISE_OK) return st;
+  char *w = static_cast<char *>(ws);
+  FinishParams p{};
+  p.rows = a->rows;
+  p.heads = a->heads;
+  p.head_dim = a->head_dim;
+  p.max_blocks = L.max_blocks;
+  p.items_per_unit = L.items_per_unit;
+  p.ctx_len = a->ctx_len;
+  p.out = a->out;
+  p.row_code = reinterpret_cast<const int32_t *>(w + L.off_row_code);
+  p.unit_items = reinterpret_cast<const int32_t *>(w + L.off_unit_items);
+  p.part_ml = reinterpret_cast<const float2 *>(w + L.off_part_ml);
+  p.part_acc = reinterpret_cast<const float *>(w + L.off_part_acc);
+  p.stats = reinterpret_cast<const float2 *>(w + L.off_stats);
+  if (s) {
+    p.support = s->support;
+    p.slots = s->slots;
+    p.layers = s->layers;
+    p.layer = s->layer;
+    p.words = s->words;
+    p.slot_of_row = s->slot_of_row;
+    p.tags = s->tags;
+    p.row_request = s->row_request;
+    p.row_position = s->row_position;
+    p.eta = s->eta;
+    p.counters = reinterpret_cast<unsigned long long *>(s->counters);
+  }
+  if (launch_finish(p, static_cast<hipStream_t>(stream)) != hipSuccess) return WISE_E_HIP;
+  return WISE_OK;
+}
+
+const char *wise_status_string(wise_status st) {
+  switch (st) {
+    case WISE_OK: return "ok";
+    case WISE_E_ARG: return "invalid argument";
+    case WISE_E_UNSUPPORTED: return "unsupported size, dtype or layout";
+    case WISE_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case WISE_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

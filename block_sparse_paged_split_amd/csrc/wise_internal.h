@@ -1,0 +1,88 @@
+// Internal declarations shared by the split-KV kernel, the finish kernel and
+// the host entry points of libwise.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "wise.h"
+
+namespace wise {
+
+constexpr int kBlock = WISE_BLOCK;     // tokens per tile / selection block
+constexpr int kWavesPerGroup = 4;      // waves per split workgroup (one work item each)
+constexpr int kMaxTilesPerItem = 16;   // upper bound of tiles per work item
+constexpr int kMaxCtx = 65536;         // tokens; 2048 blocks, 64 support words
+constexpr int kMaxBlocks = kMaxCtx / kBlock;
+constexpr int kMaxWords = kMaxBlocks / 32;
+constexpr int kFinishThreads = 256;
+constexpr int kMaxItemsPerUnit = 512;  // kMaxBlocks / smallest tiles-per-item (4)
+constexpr int kRowError = 0xF;         // row code: bad device data for the row
+
+// Row code written by the split kernel (wave of head 0, item 0) and read by
+// the finish kernel: effective mode in bits 0..3 (kRowError for a bad row),
+// requested mode in bits 4..7.
+__host__ __device__ inline int encode_row(int eff, int req) { return (eff & 0xF) | ((req & 0xF) << 4); }
+
+// Work decomposition: unit = (row, head); a unit's attended tiles (all causal
+// tiles, or the support's tiles in ascending order) are cut into work items of
+// tiles_per_item consecutive list entries.  One wave per item slot.
+int tiles_per_item(int max_blocks);
+
+struct Layout {
+  int rows, heads, head_dim, max_ctx, max_blocks, tiles_per_item, items_per_unit;
+  size_t off_row_code, off_unit_items, off_part_ml, off_part_acc, off_stats, total;
+};
+// Returns false if the sizes are outside the supported range.
+bool make_layout(int rows, int heads, int head_dim, int max_ctx, Layout *L);
+
+struct SplitParams {
+  const void *q, *k, *v;
+  int64_t stride_page_b, stride_head_b, stride_token_b;  // bytes
+  const int32_t *block_table;
+  int64_t bt_stride;
+  const int32_t *ctx_len;
+  int32_t rows, heads, max_ctx, max_blocks, num_pages, page_shift;
+  float qk_scale_log2;  // softmax scale * log2(e)
+  int32_t tiles_per_item, items_per_unit, chunk_groups;
+  // requested modes
+  const uint8_t *row_mode;  // NULL: every row uniform_mode
+  int32_t uniform_mode;
+  // support state (unused when every row is DENSE)
+  const uint32_t *support;
+  int32_t slots, layers, layer, words, required;
+  const int32_t *slot_of_row;
+  const wise_tag *tags;
+  const int64_t *row_request, *row_position;
+  unsigned long long *counters;
+  // workspace and optional export
+  int32_t *row_code, *unit_items;
+  float2 *part_ml;
+  float *part_acc;
+  float2 *stats;
+  float2 *stats_export;
+};
+
+struct FinishParams {
+  int32_t rows, heads, head_dim, max_blocks, items_per_unit;
+  const int32_t *ctx_len;
+  float *out;
+  const int32_t *row_code, *unit_items;
+  const float2 *part_ml;
+  const float *part_acc;
+  const float2 *stats;
+  // support state; support == NULL after a dense-only call
+  uint32_t *support;
+  int32_t slots, layers, layer, words;
+  const int32_t *slot_of_row;
+  wise_tag *tags;
+  const int64_t *row_request, *row_position;
+  float eta;
+  unsigned long long *counters;
+};
+
+hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_finish(const FinishParams &p, hipStream_t stream);
+
+}  // namespace wise

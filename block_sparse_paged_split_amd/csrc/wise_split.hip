@@ -1,0 +1,361 @@
+// Split-KV paged decode attention with per-row modes (dense / discover /
+// discover-union / sparse) for gfx950.
+//
+// WISE pull request page (vllm-rlt pull 143), "What changes": one split-KV
+// paged decode kernel with per-row modes -- dense; discover = dense while
+// recording each 32-token tile's max and sum; sparse = only the row's
+// selected tiles, compacted first so the loop has no branch -- whose
+// programs each cover about eight tiles, so a long dense row does not set
+// the latency of a launch whose other rows are sparse.
+//
+// MI355X design:
+//  * One wave64 per work item (<= tiles_per_item consecutive entries of a
+//    (row, head)'s tile list); four independent waves per workgroup; the grid
+//    covers every (unit, item) slot, and each wave plans its own item (tag
+//    check, fallback, tile count, compacted tile list) so that a call is a
+//    single launch with no host readback.
+//  * A 32-token K (or V) tile is read with 16-byte loads in which each load
+//    instruction covers TPI whole tokens contiguously (1 KB per wave for
+//    bf16 d=128): lane = (token subgroup g, 16-byte dim chunk c).  Every K
+//    and V load of a tile is issued before any arithmetic.
+//  * q.k uses v_dot2 (bf16 pairs, fp32 accumulate) or fp32 FMA, reduced
+//    across the LPT lanes of a token with DPP row rotations.  Online softmax
+//    runs in base 2 on scores pre-scaled by scale*log2(e).  Every reduction
+//    is a fixed butterfly, so all lanes hold bitwise-identical statistics and
+//    a row's result does not depend on the other rows of the launch.
+#include "wise_internal.h"
+
+namespace wise {
+
+namespace {
+
+constexpr float kLn2 = 0.693147180559945309417f;
+
+template <bool kBf16, int D>
+struct Geo {
+  static constexpr int E = kBf16 ? 2 : 4;       // bytes per element
+  static constexpr int BPT = D * E;             // bytes per token row
+  static constexpr int LPT = BPT / 16;          // lanes per token (16 B each)
+  static constexpr int TPI = 64 / LPT;          // tokens per load instruction
+  static constexpr int NI = kBlock / TPI;       // load instructions per tile
+  static constexpr int EPL = 16 / E;            // elements per lane per load
+  static_assert(LPT >= 8 && LPT <= 32, "unsupported head_dim/dtype");
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of LPT consecutive lanes; every lane of a group
+// gets the bitwise-same total.
+template <int LPT>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  if constexpr (LPT == 8) {
+    x += dpp<0x141>(x);  // row_half_mirror
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  } else {
+    x += dpp<0x128>(x);  // row_ror:8
+    x += dpp<0x124>(x);  // row_ror:4
+    x += dpp<0x122>(x);  // row_ror:2
+    x += dpp<0x121>(x);  // row_ror:1
+    if constexpr (LPT == 32) x += __shfl_xor(x, 16);
+  }
+  return x;
+}
+
+// Combine across the TPI token subgroups (lanes l, l ^ LPT, l ^ 2 LPT, ...).
+template <int LPT>
+__device__ __forceinline__ float subgroup_max(float x) {
+  if constexpr (LPT <= 8) x = fmaxf(x, dpp<0x128>(x));  // partner lane l ^ 8 within the row
+  if constexpr (LPT <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+template <int LPT>
+__device__ __forceinline__ float subgroup_sum(float x) {
+  if constexpr (LPT <= 8) x += dpp<0x128>(x);
+  if constexpr (LPT <= 16) x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+
+// Dot product of one lane's 16 bytes of K with the same 16 bytes of q.
+// (Whole-vector bit casts: casting a single swizzled element of an
+// ext_vector into a bf16 vector is miscompiled by this toolchain.)
+template <bool kBf16>
+__device__ __forceinline__ float dot16(u32x4 k, u32x4 q) {
+  if constexpr (kBf16) {
+    const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, k);
+    const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, q);
+    float a = __builtin_amdgcn_fdot2_f32_bf16(kb.s01, qb.s01, 0.0f, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(kb.s23, qb.s23, a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(kb.s45, qb.s45, a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(kb.s67, qb.s67, a, false);
+    return a;
+  } else {
+    float a = __uint_as_float(k[0]) * __uint_as_float(q[0]);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) a = fmaf(__uint_as_float(k[i]), __uint_as_float(q[i]), a);
+    return a;
+  }
+}
+
+// acc[0..EPL) += w * v (the lane's EPL elements of one token's V row);
+// bf16 element 2i is the low half of word i, element 2i+1 the high half.
+template <bool kBf16>
+__device__ __forceinline__ void axpy16(float *acc, float w, u32x4 v) {
+  if constexpr (kBf16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = v[i];
+      acc[2 * i] = fmaf(w, bf16_lo(x), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(w, bf16_hi(x), acc[2 * i + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, __uint_as_float(v[i]), acc[i]);
+  }
+}
+
+__device__ __forceinline__ u32x4 load16(const char *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+template <bool kBf16, int D>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void split_kernel(const SplitParams p) {
+  using G = Geo<kBf16, D>;
+  __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u = blockIdx.x / p.chunk_groups;                         // unit = (row, head)
+  const int k = (blockIdx.x - u * p.chunk_groups) * kWavesPerGroup + wave;  // item slot
+  if (k >= p.items_per_unit) return;
+  const int r = u / p.heads;
+  const int h = u - r * p.heads;
+
+  // ---- plan: effective mode of the row (support tags), dense fallback ----
+  const int n = p.ctx_len[r];
+  const int req = p.row_mode ? static_cast<int>(p.row_mode[r]) : p.uniform_mode;
+  bool bad = n < 1 || n > p.max_ctx || req < WISE_DENSE || req > WISE_SPARSE;
+  int eff = req, slot = r;
+  bool fallback = false;
+  if (!bad && req != WISE_DENSE) {
+    if (p.slot_of_row) slot = p.slot_of_row[r];
+    if (slot < 0 || slot >= p.slots) {
+      bad = true;
+    } else if (req == WISE_DISCOVER_UNION || req == WISE_SPARSE) {
+      const wise_tag *t = p.tags + static_cast<int64_t>(slot) * p.layers + p.layer;
+      const bool same = t->request == p.row_request[r] && t->position == p.row_position[r];
+      const int need = req == WISE_SPARSE ? p.required : 1;
+      if (!(same && t->discoveries >= need)) {
+        eff = WISE_DENSE;
+        fallback = true;
+      }
+    }
+  }
+
+  // ---- tile count: all causal tiles, or the support's set bits ----
+  const int nb = bad ? 0 : (n + kBlock - 1) / kBlock;
+  const bool sparse = !bad && eff == WISE_SPARSE;
+  int count = nb;
+  uint32_t word = 0;
+  int incl = 0;
+  if (sparse) {
+    const uint32_t *sw =
+        p.support + ((static_cast<int64_t>(slot) * p.layers + p.layer) * p.heads + h) * p.words;
+    const int nw = (nb + 31) >> 5;
+    if (lane < nw) {
+      word = sw[lane];
+      const int valid = nb - 32 * lane;
+      if (valid < 32) word &= (1u << valid) - 1u;
+    }
+    incl = wave_inclusive_scan(__popc(word), lane);
+    count = __builtin_amdgcn_readlane(incl, 63);
+  }
+  const int T = p.tiles_per_item;
+  const int items = bad ? 0 : (count + T - 1) / T;
+  if (k == 0 && lane == 0) {
+    p.unit_items[u] = items;
+    if (h == 0) {
+      p.row_code[r] = encode_row(bad ? kRowError : eff, req);
+      if (fallback && p.counters) atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
+    }
+  }
+  if (k >= items) return;
+
+  const int first = k * T;
+  const int ntiles = min(T, count - first);
+
+  // ---- compact this item's slice of the support into a tile list ----
+  if (sparse) {
+    const int excl = incl - __popc(word);
+    const unsigned long long past = __builtin_amdgcn_ballot_w64(incl > first);
+    int w = __builtin_amdgcn_readfirstlane(__builtin_ctzll(past));
+    int got = 0;
+    while (got < ntiles) {
+      const uint32_t wv = __builtin_amdgcn_readlane(word, w);
+      const int base = __builtin_amdgcn_readlane(excl, w);
+      const bool set = lane < 32 && ((wv >> (lane & 31)) & 1u);
+      const unsigned long long bm = __builtin_amdgcn_ballot_w64(set);
+      const int rank = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0));
+      if (set && rank >= first && rank < first + ntiles) s_tiles[wave][rank - first] = 32 * w + lane;
+      got = min(ntiles, base + __popcll(bm) - first);
+      ++w;
+    }
+    // the list is read back by every lane of this wave below
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- per-lane constants ----
+  const int c = lane % G::LPT;  // 16-byte dim chunk: elements [c*EPL, c*EPL+EPL)
+  const int g = lane / G::LPT;  // token subgroup: token j*TPI + g of load j
+  const uint32_t lane_off = static_cast<uint32_t>(g * p.stride_token_b + c * 16);
+  const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) +
+                                                    (static_cast<int64_t>(u) * D + c * G::EPL) * G::E);
+  const char *kh = static_cast<const char *>(p.k) + h * p.stride_head_b;  // wave-uniform
+  const char *vh = static_cast<const char *>(p.v) + h * p.stride_head_b;
+  const int32_t *bt = p.block_table + r * p.bt_stride;
+  const int pmask = (1 << p.page_shift) - 1;
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  float acc[G::EPL];
+#pragma unroll
+  for (int e = 0; e < G::EPL; ++e) acc[e] = 0.0f;
+  float st_m = 0.0f, st_l = 0.0f;  // tile stats of list entry `lane`
+  bool page_err = false;
+
+  // Physical page of load instruction j of tile (list entry) i: lane j of a
+  // page vector fetched one tile ahead.  A load instruction whose tokens are
+  // all past the context reuses the page of the row's last token with the
+  // slot offset it would have had, which stays inside that page; its lanes
+  // are masked below.
+  auto tile_of = [&](int i) -> int {
+    return sparse ? __builtin_amdgcn_readfirstlane(s_tiles[wave][i]) : first + i;
+  };
+  auto fetch_pages = [&](int b) -> int {
+    const int tj = b * kBlock + min(lane, G::NI - 1) * G::TPI;
+    return bt[min(tj, n - 1) >> p.page_shift];
+  };
+  int pages_next = fetch_pages(tile_of(0));
+
+  for (int i = 0; i < ntiles; ++i) {
+    const int b = tile_of(i);
+    const int t0 = b * kBlock;
+    const int nv = min(kBlock, n - t0);  // valid tokens in this tile (>= 1)
+    const int pages = pages_next;
+    if (i + 1 < ntiles) pages_next = fetch_pages(tile_of(i + 1));
+
+    // issue every K and V load of the tile before any arithmetic
+    u32x4 kr[G::NI], vr[G::NI];
+#pragma unroll
+    for (int j = 0; j < G::NI; ++j) {
+      int page = __builtin_amdgcn_readlane(pages, j);
+      const bool pbad = static_cast<unsigned>(page) >= static_cast<unsigned>(p.num_pages);
+      page_err |= pbad;
+      page = pbad ? 0 : page;
+      const int64_t off = page * p.stride_page_b + ((t0 + j * G::TPI) & pmask) * p.stride_token_b;
+      kr[j] = load16(kh + off + lane_off);
+      vr[j] = load16(vh + off + lane_off);
+    }
+    // keep all 2*NI loads in flight together: no arithmetic moves above here
+    __builtin_amdgcn_sched_barrier(0);
+
+    // scores of this lane's NI tokens (base-2 units)
+    float s[G::NI];
+#pragma unroll
+    for (int j = 0; j < G::NI; ++j) {
+      const float d = lane_group_sum<G::LPT>(dot16<kBf16>(kr[j], qv));
+      s[j] = (j * G::TPI + g < nv) ? d * p.qk_scale_log2 : -INFINITY;
+    }
+    float mb = s[0];
+#pragma unroll
+    for (int j = 1; j < G::NI; ++j) mb = fmaxf(mb, s[j]);
+    mb = subgroup_max<G::LPT>(mb);
+    float pj[G::NI], ls = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G::NI; ++j) {
+      pj[j] = __builtin_amdgcn_exp2f(s[j] - mb);
+      ls += pj[j];
+    }
+    const float lb = subgroup_sum<G::LPT>(ls);
+    if (lane == i) {
+      st_m = mb;
+      st_l = lb;
+    }
+
+    // online-softmax update of this item's running (m, l, acc)
+    const float m_new = fmaxf(m_run, mb);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float beta = __builtin_amdgcn_exp2f(mb - m_new);
+    l_run = l_run * alpha + lb * beta;
+#pragma unroll
+    for (int e = 0; e < G::EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < G::NI; ++j) {
+      const bool valid = j * G::TPI + g < nv;
+      const u32x4 v = valid ? vr[j] : u32x4{0u, 0u, 0u, 0u};
+      axpy16<kBf16>(acc, pj[j] * beta, v);
+    }
+    m_run = m_new;
+  }
+
+  // ---- partial (m, l, acc) of this item, and the tile stats ----
+#pragma unroll
+  for (int e = 0; e < G::EPL; ++e) acc[e] = subgroup_sum<G::LPT>(acc[e]);
+  const int64_t slot_idx = static_cast<int64_t>(u) * p.items_per_unit + k;
+  if (g == 0) {
+    float4 *dst = reinterpret_cast<float4 *>(p.part_acc + slot_idx * D + c * G::EPL);
+#pragma unroll
+    for (int e = 0; e < G::EPL; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  }
+  if (lane == 0) p.part_ml[slot_idx] = page_err ? make_float2(0.0f, -1.0f) : make_float2(m_run, l_run);
+  if (lane < ntiles) {
+    const int b = sparse ? s_tiles[wave][lane] : first + lane;
+    const int64_t si = static_cast<int64_t>(u) * p.max_blocks + b;
+    p.stats[si] = make_float2(st_m, st_l);
+    if (p.stats_export) p.stats_export[si] = make_float2(st_m * kLn2, st_l);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
+  const dim3 block(64 * kWavesPerGroup);
+  if (dtype == WISE_BF16 && head_dim == 128) {
+    hipLaunchKernelGGL((split_kernel<true, 128>), grid, block, 0, stream, p);
+  } else if (dtype == WISE_BF16 && head_dim == 64) {
+    hipLaunchKernelGGL((split_kernel<true, 64>), grid, block, 0, stream, p);
+  } else if (dtype == WISE_F32 && head_dim == 128) {
+    hipLaunchKernelGGL((split_kernel<false, 128>), grid, block, 0, stream, p);
+  } else if (dtype == WISE_F32 && head_dim == 64) {
+    hipLaunchKernelGGL((split_kernel<false, 64>), grid, block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wise

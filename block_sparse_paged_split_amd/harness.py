@@ -1,0 +1,188 @@
+"""Device-side plumbing around the binding: upload synthetic inputs, hold the
+support state, run one (depth, layer) call, time with HIP events.
+
+PyTorch supplies device memory and the stream; every computation of the
+method runs in libwise's kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+from . import synth
+from . import wise as W
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(x: np.ndarray, device, dtype: Optional[str] = None):
+    """numpy -> torch on device; bf16 bit patterns (uint16) become bfloat16."""
+    torch = _torch()
+    if x.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device)
+
+
+@dataclasses.dataclass
+class DeviceLayer:
+    """Encoded inputs and outputs of one (depth, layer) call on the device."""
+
+    q: object
+    k: object
+    v: object
+    block_table: object
+    ctx_len: object
+    out: object
+    tile_stats: Optional[object]
+    page_size: int
+    max_ctx: int
+
+    def attn(self, events=None) -> W.WiseAttn:
+        return W.attn_from(self.q, self.k, self.v, self.block_table, self.ctx_len, self.out,
+                           page_size=self.page_size, max_ctx=self.max_ctx,
+                           tile_stats=self.tile_stats, events=events)
+
+    @property
+    def kv_bytes(self) -> int:
+        return int(self.k.numel() * self.k.element_size() * 2)
+
+
+def upload(li: synth.LayerInputs, device="cuda", with_stats: bool = False) -> DeviceLayer:
+    torch = _torch()
+    w = li.workload
+    R, H, d = li.q.shape
+    nbmax = (w.max_ctx + synth.BLOCK - 1) // synth.BLOCK
+    return DeviceLayer(
+        q=to_device(li.q, device), k=to_device(li.k, device), v=to_device(li.v, device),
+        block_table=to_device(li.block_table, device), ctx_len=to_device(li.ctx_len, device),
+        out=torch.empty((R, H, d), dtype=torch.float32, device=device),
+        tile_stats=(torch.full((R, H, nbmax, 2), float("nan"), dtype=torch.float32, device=device)
+                    if with_stats else None),
+        page_size=w.page_size, max_ctx=w.max_ctx)
+
+
+class SupportState:
+    """Support bitmask, tags and counters of a workload (the pages' WiseState)."""
+
+    def __init__(self, rows: int, heads: int, max_ctx: int, layers: int = 1, device="cuda",
+                 slots: Optional[int] = None):
+        torch = _torch()
+        self.slots = rows if slots is None else slots
+        nb = (max_ctx + synth.BLOCK - 1) // synth.BLOCK
+        self.words = (nb + 31) // 32
+        self.support = torch.zeros((self.slots, layers, heads, self.words), dtype=torch.int32, device=device)
+        self.tags = torch.zeros((self.slots, layers, 3), dtype=torch.int64, device=device)
+        self.counters = torch.zeros(W.NUM_COUNTERS, dtype=torch.int64, device=device)
+        self.row_request = torch.arange(rows, dtype=torch.int64, device=device) + 1000
+        self.row_position = torch.zeros(rows, dtype=torch.int64, device=device)
+        self.slot_of_row = None
+
+    def view(self, layer: int, required: int, eta: float) -> W.WiseSupport:
+        return W.support_from(self.support, self.tags, layer=layer, row_request=self.row_request,
+                              row_position=self.row_position, required=required, eta=eta,
+                              counters=self.counters, slot_of_row=self.slot_of_row)
+
+    def tags_numpy(self):
+        """Tags as the oracle's structured dtype."""
+        raw = self.tags.cpu().numpy().copy()
+        out = np.zeros(raw.shape[:2], dtype=[("request", "<i8"), ("position", "<i8"),
+                                             ("discoveries", "<i4"), ("reserved", "<i4")])
+        out["request"] = raw[..., 0]
+        out["position"] = raw[..., 1]
+        out["discoveries"] = (raw[..., 2] & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+        return out
+
+    def support_numpy(self):
+        return self.support.cpu().numpy().view(np.uint32)
+
+
+class Workspace:
+    def __init__(self, rows, heads, head_dim, max_ctx, device="cuda"):
+        torch = _torch()
+        self.nbytes = W.wise_workspace_size(rows, heads, head_dim, max_ctx)
+        if self.nbytes == 0:
+            raise ValueError("unsupported sizes for libwise")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        assert self.buf.data_ptr() % 256 == 0
+
+    @property
+    def ptr(self) -> int:
+        return int(self.buf.data_ptr())
+
+
+def stream_handle() -> int:
+    return int(_torch().cuda.current_stream().cuda_stream)
+
+
+def call(layer: DeviceLayer, ws: Workspace, mode: int, state: Optional[SupportState] = None,
+         layer_idx: int = 0, required: int = 2, eta: float = 0.95, row_mode=None,
+         events=None, stream: Optional[int] = None) -> None:
+    """One (depth, layer) call: decode (split-KV kernel) + finish."""
+    st = stream_handle() if stream is None else stream
+    a = layer.attn(events)
+    s = state.view(layer_idx, required, eta) if state is not None else None
+    if row_mode is not None:
+        W.wise_decode_sparse(a, s, int(row_mode.data_ptr()), ws.ptr, ws.nbytes, st)
+    elif mode == W.WISE_DENSE:
+        W.wise_decode_dense(a, ws.ptr, ws.nbytes, st)
+    elif mode in (W.WISE_DISCOVER, W.WISE_DISCOVER_UNION):
+        W.wise_decode_discover(a, s, mode == W.WISE_DISCOVER_UNION, ws.ptr, ws.nbytes, st)
+    else:
+        W.wise_decode_sparse(a, s, None, ws.ptr, ws.nbytes, st)
+    W.wise_finish_select(a, s, ws.ptr, ws.nbytes, st)
+
+
+class HipEvents:
+    """Raw HIP events (hipEventCreate) usable as the library's timing hook."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+
+    def handle(self, i: int) -> int:
+        return int(self.ev[i].value)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            for e in self.ev:
+                self.hip.hipEventDestroy(e)
+        except Exception:
+            pass
+
+
+class EventPair:
+    """(begin, end) handles in the shape attn_from expects (``.cuda_event``)."""
+
+    class _H:
+        def __init__(self, h):
+            self.cuda_event = h
+
+    def __init__(self, events: HipEvents, i: int, j: int):
+        self.pair = (self._H(events.handle(i)), self._H(events.handle(j)))
+
+    def __getitem__(self, k):
+        return self.pair[k]

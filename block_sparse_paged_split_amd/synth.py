@@ -82,6 +82,7 @@ class Workload:
     seed: int
     ctx: Optional[int] = None
     ctx_range: Optional[Tuple[int, int]] = None
+    ctx_list: Optional[Tuple[int, ...]] = None
     hot: Optional[int] = None
     hot_range: Optional[Tuple[int, int]] = None
     layers: int = 1
@@ -92,7 +93,11 @@ class Workload:
 
     @property
     def max_ctx(self) -> int:
-        return self.ctx if self.ctx is not None else self.ctx_range[1]
+        if self.ctx is not None:
+            return self.ctx
+        if self.ctx_list is not None:
+            return max(self.ctx_list)
+        return self.ctx_range[1]
 
     @property
     def discoveries(self) -> int:
@@ -146,6 +151,9 @@ def context_lengths(w: Workload) -> np.ndarray:
     """Per-row context lengths (tokens attended, including the current one)."""
     if w.ctx is not None:
         return np.full(w.rows, w.ctx, dtype=np.int32)
+    if w.ctx_list is not None:
+        assert len(w.ctx_list) == w.rows
+        return np.asarray(w.ctx_list, dtype=np.int32)
     lo, hi = w.ctx_range
     u = _rng(w.seed, _S_CTX).uniform(math.log(lo), math.log(hi), size=w.rows)
     return np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int32)

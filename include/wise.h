@@ -1,0 +1,197 @@
+/*
+ * wise.h -- C ABI of working-set (WISE) paged decode attention for
+ * recurrent-depth models, on AMD Instinct MI355X (gfx950).
+ *
+ * Method (WISE pull request page, InferMatrixLab/vllm-rlt pull 143,
+ * "Summary" and "What changes"): the early recurrent depths run dense
+ * split-KV decode attention over a paged KV cache and record, for every
+ * 32-token tile, the softmax max and sum; a finish step merges the splits
+ * and, for discovery rows, selects per (row, layer, head) the support: the
+ * fewest tiles, heaviest first, whose softmax mass reaches eta (0.95 by
+ * default), ORed across discovery depths.  Later depths attend only the
+ * selected tiles, with Q/K/V and the softmax weights inside the support
+ * recomputed.  Support lives in a [slot, layer, head, block] bitmask that
+ * is tagged with the (request, position) it was discovered for; a row whose
+ * discovery is missing or incomplete attends densely and is counted as a
+ * fallback.
+ *
+ * Call sequence per (depth, layer):
+ *     wise_decode_dense | wise_decode_discover | wise_decode_sparse
+ *     wise_finish_select            (same workspace, same stream, next)
+ * The decode call runs the split-KV kernel (one launch, every row mode);
+ * the finish call merges the splits into `out`, runs the eta selection for
+ * discovery rows, updates the bitmask, the tags and the counters.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers owned by the caller; they are
+ *     borrowed until the enqueued work completes.  Scalars are host values.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is only
+ *     enqueued; nothing is synchronised, nothing is allocated, no host
+ *     state is kept, so calls are re-entrant and capturable in HIP graphs.
+ *   - Host-checkable arguments are validated before anything is enqueued;
+ *     on any error nothing is enqueued and the status says why.
+ *   - Device data that cannot be checked without a sync (a context length
+ *     outside [1, max_ctx], a page id outside [0, num_pages), a slot id
+ *     outside [0, slots), a row mode outside the enum, an empty support)
+ *     makes the affected (row, head) output NaN; wise_finish_select adds
+ *     one to counters[WISE_CTR_ERRORS] per such (row, head).
+ *   - Two calls that share a workspace must be ordered (same stream).
+ *     Rows of one call must map to distinct slots.
+ */
+#ifndef WISE_H
+#define WISE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Tokens per tile and per selection block (the method's B = 32). */
+#define WISE_BLOCK 32
+
+typedef enum wise_status {
+  WISE_OK = 0,
+  WISE_E_ARG = 1,          /* a null required pointer or an out-of-range scalar */
+  WISE_E_UNSUPPORTED = 2,  /* head_dim, dtype, page_size or a size limit not supported */
+  WISE_E_WORKSPACE = 3,    /* ws is NULL/misaligned or ws_bytes < wise_workspace_size() */
+  WISE_E_HIP = 4           /* a HIP launch or event call failed */
+} wise_status;
+
+/* Requested per-row mode (a uint8 per row in wise_decode_sparse's row_mode). */
+typedef enum wise_mode {
+  WISE_DENSE = 0,           /* plain paged decode attention, no state touched */
+  WISE_DISCOVER = 1,        /* dense + tile stats; selection replaces the support */
+  WISE_DISCOVER_UNION = 2,  /* dense + tile stats; selection is ORed into the support */
+  WISE_SPARSE = 3           /* attend only the support's tiles */
+} wise_mode;
+
+typedef enum wise_dtype { WISE_BF16 = 0, WISE_F32 = 1 } wise_dtype;
+
+/* Indices into the counters array (uint64 each, accumulated, never reset). */
+enum {
+  WISE_CTR_FALLBACKS = 0,   /* rows that requested UNION/SPARSE and ran dense */
+  WISE_CTR_SELECTED = 1,    /* union blocks: DISCOVER adds K, UNION adds newly set bits */
+  WISE_CTR_CAUSAL = 2,      /* causal blocks of DISCOVER units */
+  WISE_CTR_ERRORS = 3,      /* (row, head) units whose output was set to NaN */
+  WISE_NUM_COUNTERS = 4
+};
+
+/*
+ * Support tag of one (slot, layer): the discovery window the support words
+ * of that (slot, layer) hold.  discoveries = 0 means released / invalid.
+ * A DISCOVER row sets {request, position, 1}; a DISCOVER_UNION row needs
+ * {request, position} to match with discoveries >= 1 and adds one; a
+ * SPARSE row needs them to match with discoveries >= discoveries_required.
+ * A DISCOVER_UNION row whose window is broken runs dense and sets
+ * discoveries = 0, so the rest of that token runs dense too.
+ */
+typedef struct wise_tag {
+  int64_t request;
+  int64_t position;
+  int32_t discoveries;
+  int32_t reserved;
+} wise_tag; /* 24 bytes */
+
+/*
+ * Attention operands of one (depth, layer) call.
+ *   q         [rows, heads, head_dim], contiguous, dtype.
+ *   k_cache,  element (page, head, slot, dim) at
+ *   v_cache     page*stride_page + head*stride_head + slot*stride_token + dim
+ *             (element strides; dim is contiguous).  [pages, heads, P, d] has
+ *             strides (heads*P*d, P*d, d); [pages, P, heads, d] has
+ *             (P*heads*d, d, heads*d).  Pointers and every stride in bytes
+ *             must be multiples of 16.
+ *   block_table [rows, bt_stride] int32: logical page j of row r is physical
+ *             page block_table[r*bt_stride + j]; bt_stride >= ceil(max_ctx/P).
+ *             Only entries below ceil(ctx_len[r]/P) are read.
+ *   ctx_len   [rows] int32, tokens attended (including the current one).
+ *   max_ctx   host bound on ctx_len, sizes the grid and the workspace.
+ *   scale     softmax scale; 0 selects 1/sqrt(head_dim).
+ *   out       [rows, heads, head_dim] fp32, written by wise_finish_select.
+ *   tile_stats optional [rows, heads, ceil(max_ctx/32), 2] fp32: for every
+ *             tile a row attends, (max scaled score, sum exp(score - max))
+ *             in natural-log units; other entries are left untouched.
+ *   ev_split_begin/end optional hipEvent_t recorded on `stream` right
+ *             before and after the split-KV kernel (timing hook), or NULL.
+ * Supported: head_dim 64 or 128; page_size a power of two in [8, 4096];
+ * max_ctx <= 65536; rows*heads <= 2^22.
+ */
+typedef struct wise_attn {
+  int32_t rows, heads, head_dim, dtype;
+  const void *q;
+  const void *k_cache, *v_cache;
+  int64_t stride_page, stride_head, stride_token;
+  int32_t num_pages, page_size;
+  const int32_t *block_table;
+  int32_t bt_stride;
+  const int32_t *ctx_len;
+  int32_t max_ctx;
+  float scale;
+  float *out;
+  float *tile_stats;
+  void *ev_split_begin, *ev_split_end;
+} wise_attn;
+
+/*
+ * Support state (the pages' WiseState) and the per-call selection inputs.
+ *   support   [slots, layers, heads, words] uint32; bit b of a (slot, layer,
+ *             head) is bit (b % 32) of word (b / 32).
+ *             words >= ceil(ceil(max_ctx/32)/32).
+ *   layer     the layer of this call, in [0, layers).
+ *   slot_of_row [rows] int32 or NULL (row r uses slot r).
+ *   tags      [slots, layers] wise_tag.
+ *   row_request, row_position [rows] int64: the token each row decodes.
+ *   discoveries_required  discovery depths a SPARSE row needs (>= 1).
+ *   eta       cumulative-mass target in (0, 1].
+ *   counters  [WISE_NUM_COUNTERS] uint64 or NULL.
+ */
+typedef struct wise_support {
+  uint32_t *support;
+  int32_t slots, layers, words, layer;
+  const int32_t *slot_of_row;
+  wise_tag *tags;
+  const int64_t *row_request, *row_position;
+  int32_t discoveries_required;
+  float eta;
+  uint64_t *counters;
+} wise_support;
+
+/* Bytes of workspace a call with these sizes needs (0 if unsupported). */
+size_t wise_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t max_ctx);
+
+/* Every row DENSE.  No support state is read or written.  Follow with
+ * wise_finish_select(a, NULL, ...). */
+wise_status wise_decode_dense(const wise_attn *a, void *ws, size_t ws_bytes, void *stream);
+
+/* Every row DISCOVER (union_with_previous == 0) or DISCOVER_UNION (!= 0):
+ * dense attention that also records every tile's (max, sum).  Follow with
+ * wise_finish_select(a, s, ...), which selects and updates the state. */
+wise_status wise_decode_discover(const wise_attn *a, const wise_support *s,
+                                 int32_t union_with_previous, void *ws, size_t ws_bytes,
+                                 void *stream);
+
+/* Every row SPARSE (row_mode == NULL), or per-row modes from the device
+ * array row_mode [rows] uint8 (one launch mixes dense, discover, union and
+ * sparse rows).  Sparse rows walk only the tiles of their support, whose
+ * list is compacted before the loop.  Follow with wise_finish_select(a, s). */
+wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
+                               const uint8_t *row_mode, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/* Merge the splits of the preceding decode call into a->out; for discovery
+ * rows run the eta selection, write/OR the support, update the tags and
+ * the counters.  `a` and `s` must describe the same call as the decode
+ * call (s == NULL after wise_decode_dense). */
+wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/* Static, human-readable name of a status. */
+const char *wise_status_string(wise_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WISE_H */

@@ -1,0 +1,133 @@
+"""GPU-vs-oracle comparison of one (depth, layer) call.
+
+The oracle is evaluated from the GPU's own pre-call state (support bitmask,
+tags), so every call is checked on its own: outputs of dense / discover rows
+against plain attention, outputs of sparse rows against masked attention
+over the support the GPU itself holds, and the post-call support against
+the oracle's selection (bit-exact, except units whose cut lies within 1e-6
+of eta, or whose K-th and (K+1)-th masses tie within 1e-6 relative: those
+are counted and returned).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+
+from oracle import wise_oracle as O
+from block_sparse_paged_split_amd import harness, synth
+from block_sparse_paged_split_amd import wise as W
+
+TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
+
+
+@dataclasses.dataclass
+class Report:
+    max_abs: float = 0.0
+    max_rel: float = 0.0
+    units: int = 0
+    near_eta: int = 0          # class A: exempt support mismatches possible
+    near_tie: int = 0          # class B
+    support_mismatch: int = 0  # mismatching units (must be <= near_eta + near_tie)
+    counters: Optional[np.ndarray] = None
+
+
+def assert_close(got, ref, dtype, what, report: Report):
+    atol, rtol = TOL[dtype]
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), f"{what}: NaN pattern differs"
+    g, r = got[~nan_ref], ref[~nan_ref]
+    if g.size == 0:
+        return
+    err = np.abs(g - r)
+    report.max_abs = max(report.max_abs, float(err.max()))
+    report.max_rel = max(report.max_rel, float((err / np.maximum(np.abs(r), 1e-30)).max()))
+    bad = err > atol + rtol * np.abs(r)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of tolerance; "
+                           f"max abs {err.max():.3e}")
+
+
+def check_call(w: synth.Workload, li: synth.LayerInputs, dev: harness.DeviceLayer,
+               ws: harness.Workspace, state: Optional[harness.SupportState], *, mode: int,
+               row_modes: Optional[np.ndarray] = None, layer: int = 0,
+               rows: Optional[Sequence[int]] = None, required: Optional[int] = None,
+               eta: Optional[float] = None, check_stats: bool = True) -> Report:
+    import torch
+    R = li.q.shape[0]
+    required = w.discoveries if required is None else required
+    eta = w.eta if eta is None else eta
+    rows = list(range(R)) if rows is None else list(rows)
+    sup0 = state.support_numpy().copy() if state else None
+    tags0 = state.tags_numpy() if state else None
+    ctr0 = state.counters.cpu().numpy().copy() if state else None
+    rm_dev = None
+    if row_modes is not None:
+        rm_dev = torch.from_numpy(row_modes.astype(np.uint8)).to(dev.q.device)
+    harness.call(dev, ws, mode, state, layer_idx=layer, required=required, eta=eta, row_mode=rm_dev)
+    torch.cuda.synchronize()
+    out = dev.out.cpu().numpy()
+    modes = row_modes if row_modes is not None else np.full(R, mode)
+    kw = {}
+    if state:
+        kw = dict(support=sup0, tags=tags0, layer=layer,
+                  slot_of_row=None if state.slot_of_row is None else state.slot_of_row.cpu().numpy(),
+                  row_request=state.row_request.cpu().numpy(),
+                  row_position=state.row_position.cpu().numpy(), required=required, eta=eta)
+    ref = O.run_call(q=li.q, k_cache=li.k, v_cache=li.v, block_table=li.block_table,
+                     ctx_len=li.ctx_len, page_size=w.page_size, num_pages=li.num_pages,
+                     max_ctx=w.max_ctx, modes=modes, rows=rows, **kw)
+    rep = Report()
+    for r in rows:
+        assert_close(out[r], ref.out[r], w.dtype, f"row {r} output", rep)
+    rep.units = len(rows) * w.heads
+    if state is None:
+        return rep
+    sup1 = state.support_numpy()
+    tags1 = state.tags_numpy()
+    ctr1 = state.counters.cpu().numpy()
+    rep.counters = ctr1 - ctr0
+    slot_of = (lambda r: r) if state.slot_of_row is None else (lambda r: int(state.slot_of_row[r]))
+    for r in rows:
+        s = slot_of(r)
+        if ref.effective[r] < 0:
+            continue
+        for h in range(w.heads):
+            unit = ref.units[(r, h)]
+            if unit.selection is not None and not unit.error:
+                same = np.array_equal(sup1[s, layer, h], ref.support[s, layer, h])
+                a = unit.selection.near_eta(eta)
+                b = unit.selection.near_tie()
+                rep.near_eta += int(a)
+                rep.near_tie += int(b and not a)
+                if not same:
+                    rep.support_mismatch += 1
+                    assert a or b, (f"support of row {r} head {h} differs: gpu "
+                                    f"{O.bits_to_blocks(sup1[s, layer, h], 2048)} oracle "
+                                    f"{unit.selection.blocks} (K={unit.selection.K}, "
+                                    f"c_K-1={unit.selection.c_prev:.9f}, c_K={unit.selection.c_K:.9f})")
+            else:
+                assert np.array_equal(sup1[s, layer, h], sup0[s, layer, h]), f"row {r} head {h} support touched"
+            if check_stats and dev.tile_stats is not None and not unit.error and unit.m is not None:
+                st = dev.tile_stats[r, h].cpu().numpy().astype(np.float64)
+                att = unit.attended
+                # tile masses relative to the oracle's row (M, L) of the attended set
+                M = np.max(unit.m)
+                Lr = np.sum(unit.l * np.exp(unit.m - M))
+                p_ref = unit.l * np.exp(unit.m - M) / Lr
+                p_gpu = st[att, 1] * np.exp(st[att, 0] - M) / Lr
+                err = np.abs(p_gpu - p_ref)
+                assert (err <= 1e-6 + 1e-5 * p_ref).all(), f"tile masses of row {r} head {h}: max {err.max():.3e}"
+        if int(modes[r]) != W.WISE_DENSE:
+            for f in ("request", "position", "discoveries"):
+                assert tags1[s, layer][f] == ref.tags[s, layer][f], f"tag {f} of row {r}"
+    if len(rows) == R:
+        assert rep.counters[W.CTR_FALLBACKS] == ref.counters[0]
+        assert rep.counters[W.CTR_ERRORS] == ref.counters[3]
+        if rep.support_mismatch == 0:
+            assert rep.counters[W.CTR_SELECTED] == ref.counters[1]
+            assert rep.counters[W.CTR_CAUSAL] == ref.counters[2]
+    return rep

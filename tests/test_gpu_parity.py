@@ -1,0 +1,240 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on the GPU.
+
+Every test prints what it runs before touching the GPU, so a failure names
+its case.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from block_sparse_paged_split_amd import harness, synth
+from block_sparse_paged_split_amd import wise as W
+from oracle import wise_oracle as O
+from parity import check_call
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    W.lib()  # fails loudly if libwise.so is missing
+    return t
+
+
+def run_schedule(w, rows=None, layer=0, eta=None, required=None, with_stats=True):
+    """All depths of w.schedule for one layer, each checked against the oracle."""
+    state = harness.SupportState(w.rows, w.heads, w.max_ctx, layers=max(w.layers, layer + 1))
+    state.row_position.fill_(17)
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    reps = []
+    for depth, mode in enumerate(w.schedule):
+        say(f"[{w.name}] depth {depth} mode {mode} layer {layer} rows {'all' if rows is None else len(rows)}")
+        li = synth.layer_inputs(w, depth, layer)
+        dev = harness.upload(li, with_stats=with_stats)
+        reps.append(check_call(w, li, dev, ws, state, mode=mode, layer=layer, rows=rows,
+                               eta=eta, required=required))
+        say(f"   max_abs {reps[-1].max_abs:.2e} near_eta {reps[-1].near_eta} "
+            f"near_tie {reps[-1].near_tie} counters {reps[-1].counters}")
+    return reps, state
+
+
+def test_tiny_f32_schedule(torch):
+    reps, state = run_schedule(synth.WORKLOADS["tiny_f32"])
+    assert reps[0].counters[W.CTR_CAUSAL] == 4 * 8
+    assert all(r.counters[W.CTR_FALLBACKS] == 0 for r in reps)
+
+
+def test_ctx1k_schedule(torch):
+    reps, state = run_schedule(synth.WORKLOADS["ctx1k"])
+    ctr = state.counters.cpu().numpy()
+    assert ctr[W.CTR_FALLBACKS] == 0 and ctr[W.CTR_ERRORS] == 0
+    assert ctr[W.CTR_CAUSAL] == 32 * 16 * 32
+    say(f"   union density {ctr[W.CTR_SELECTED] / ctr[W.CTR_CAUSAL]:.4f}")
+
+
+def test_match1k_schedule(torch):
+    """Density-matched supplement: supports far from dense."""
+    reps, state = run_schedule(synth.WORKLOADS["match1k"])
+    ctr = state.counters.cpu().numpy()
+    dens = ctr[W.CTR_SELECTED] / ctr[W.CTR_CAUSAL]
+    say(f"   union density {dens:.4f}")
+    assert dens < 0.6
+
+
+# ----------------------------------------------------------------------------- bitwise invariants
+
+def _one_layer(w, depth=0):
+    li = synth.layer_inputs(w, depth)
+    return li, harness.upload(li, with_stats=True)
+
+
+def test_modes_agree_bitwise(torch):
+    """discover output == dense output; sparse with every block == dense;
+    reruns are bitwise identical."""
+    w = synth.WORKLOADS["ctx1k"]
+    say("[ctx1k] dense / discover / all-blocks sparse, bitwise")
+    li, dev = _one_layer(w)
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    harness.call(dev, ws, W.WISE_DENSE)
+    torch.cuda.synchronize()
+    dense = dev.out.clone()
+    state = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    harness.call(dev, ws, W.WISE_DISCOVER, state, required=1)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.out, dense)
+    sup = state.support.clone()
+    for _ in range(4):
+        harness.call(dev, ws, W.WISE_DISCOVER, state, required=1)
+        torch.cuda.synchronize()
+        assert torch.equal(dev.out, dense)
+        assert torch.equal(state.support, sup)
+    state.support.fill_(-1)  # every bit set
+    harness.call(dev, ws, W.WISE_SPARSE, state, required=1)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.out, dense)
+    assert state.counters[W.CTR_FALLBACKS].item() == 0
+
+
+def test_mixed_launch_equals_uniform(torch):
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=16, name="mixed16")
+    say("[mixed16] one mixed launch vs uniform launches")
+    li0, dev0 = _one_layer(w, 0)
+    li1, dev1 = _one_layer(w, 1)
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    # reference state: every row discovered at depth 0 (for the union and sparse rows)
+    base = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    harness.call(dev0, ws, W.WISE_DISCOVER, base, required=1)
+    modes = np.array([0, 1, 2, 3] * 4, dtype=np.uint8)
+    outs = {}
+    states = {}
+    for m in range(4):
+        st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+        st.support.copy_(base.support)
+        st.tags.copy_(base.tags)
+        harness.call(dev1, ws, m, st if m else None, required=1)
+        torch.cuda.synchronize()
+        outs[m] = dev1.out.clone()
+        states[m] = st
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    st.support.copy_(base.support)
+    st.tags.copy_(base.tags)
+    harness.call(dev1, ws, W.WISE_SPARSE, st, required=1,
+                 row_mode=torch.from_numpy(modes).cuda())
+    torch.cuda.synchronize()
+    for r in range(w.rows):
+        m = int(modes[r])
+        assert torch.equal(dev1.out[r], outs[m][r]), f"row {r} mode {m}"
+        if m:
+            assert torch.equal(st.support[r], states[m].support[r])
+            assert torch.equal(st.tags[r], states[m].tags[r])
+
+
+# ----------------------------------------------------------------------------- ragged and layouts
+
+RAGGED = (1, 2, 31, 32, 33, 63, 64, 65, 100, 257, 1000)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("P", [8, 16, 32, 64])
+def test_ragged_contexts(torch, dtype, d, P):
+    w = synth.Workload(name=f"ragged_{dtype}{d}_P{P}", rows=len(RAGGED), heads=3, head_dim=d,
+                       dtype=dtype, page_size=P, shuffle=True, alpha=6.0, seed=21,
+                       ctx_list=RAGGED, hot=3, schedule=(1, 2, 3), eta=0.9)
+    run_schedule(w)
+
+
+def test_page_size_and_layout_invariance(torch):
+    """Physical layout changes nothing: same bits for page sizes 8..64, a
+    shuffled or identity block table, and [pages, P, H, d] storage."""
+    base = synth.Workload(name="layout", rows=6, heads=4, head_dim=128, dtype="bf16", page_size=8,
+                          shuffle=True, alpha=4.0, seed=5, ctx_list=(5, 40, 64, 129, 300, 511),
+                          hot=2, schedule=(1,))
+    outs = []
+    for P in (8, 16, 32, 64):
+        for shuffle in (True, False):
+            w = dataclasses.replace(base, page_size=P, shuffle=shuffle)
+            say(f"[layout] P={P} shuffle={shuffle}")
+            li = synth.layer_inputs(w, 0)
+            dev = harness.upload(li)
+            ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+            harness.call(dev, ws, W.WISE_DENSE)
+            torch.cuda.synchronize()
+            outs.append(dev.out.clone())
+            # token-major storage [pages, P, H, d], viewed as [pages, H, P, d]
+            dev.k = dev.k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+            dev.v = dev.v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+            harness.call(dev, ws, W.WISE_DENSE)
+            torch.cuda.synchronize()
+            outs.append(dev.out.clone())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+# ----------------------------------------------------------------------------- fallback and errors
+
+def test_fallback_transitions(torch):
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=8, name="fallback8")
+    say("[fallback8] broken window, release, stale position, other request")
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    li0, dev0 = _one_layer(w, 0)
+    li1, dev1 = _one_layer(w, 1)
+    li2, dev2 = _one_layer(w, 2)
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    st.row_position.fill_(5)
+    check_call(w, li0, dev0, ws, st, mode=W.WISE_DISCOVER)
+    # rows 1, 2: position moves on before the union depth (broken window)
+    st.row_position[1] = 6
+    st.row_position[2] = 6
+    rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_DISCOVER_UNION)
+    assert rep.counters[W.CTR_FALLBACKS] == 2
+    st.row_position[1] = 5
+    st.row_position[2] = 5
+    # row 3 released, row 4 stale, row 5 another request; rows 1, 2 broken above
+    tags = st.tags.clone()
+    tags[3, 0, 2] = 0
+    tags[4, 0, 1] = 4
+    tags[5, 0, 0] = 77
+    st.tags.copy_(tags)
+    rep = check_call(w, li2, dev2, ws, st, mode=W.WISE_SPARSE)
+    assert rep.counters[W.CTR_FALLBACKS] == 5
+    # incomplete window: only one discovery depth recorded of two
+    st2 = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    check_call(w, li0, dev0, ws, st2, mode=W.WISE_DISCOVER)
+    rep = check_call(w, li2, dev2, ws, st2, mode=W.WISE_SPARSE, required=2)
+    assert rep.counters[W.CTR_FALLBACKS] == w.rows
+
+
+def test_device_data_errors(torch):
+    w = synth.Workload(name="errors", rows=6, heads=2, head_dim=128, dtype="bf16", page_size=16,
+                       shuffle=True, alpha=6.0, seed=8, ctx_list=(64, 64, 64, 64, 64, 64), hot=1,
+                       schedule=(1,), eta=0.9)
+    say("[errors] bad ctx, bad page, bad mode, bad slot, empty support")
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    li = synth.layer_inputs(w, 0)
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx, slots=8)
+    dev = harness.upload(li)
+    check_call(w, li, dev, ws, st, mode=W.WISE_DISCOVER, required=1)
+    li.ctx_len = li.ctx_len.copy()
+    li.ctx_len[0] = 0                  # context outside [1, max_ctx]
+    li.block_table = li.block_table.copy()
+    li.block_table[1, 2] = li.num_pages + 5   # page id out of range, inside the context
+    dev = harness.upload(li)
+    modes = np.array([3, 3, 9, 3, 3, 3], np.uint8)   # row 2: invalid mode
+    st.slot_of_row = torch.tensor([0, 1, 2, 3, 99, 5], dtype=torch.int32, device="cuda")  # row 4: bad slot
+    sup = st.support.clone()
+    sup[5, 0, 1] = 0                   # row 5 head 1: empty support
+    st.support.copy_(sup)
+    rep = check_call(w, li, dev, ws, st, mode=W.WISE_SPARSE, row_modes=modes, required=1)
+    say(f"   counters {rep.counters}")
+    out = dev.out.cpu().numpy()
+    assert np.isnan(out[[0, 2, 4]]).all() and np.isnan(out[5, 1]).all()
+    assert not np.isnan(out[3]).any() and not np.isnan(out[5, 0]).any()
+    # row 1's bad page sits in block 1: NaN only for heads whose support holds it
