@@ -130,39 +130,62 @@ def main():
     state = harness.SupportState(w.rows, w.heads, w.max_ctx, device=dev)
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx, device=dev)
     calls = len(w.schedule) * w.layers
+    prepared = {(rep, depth): harness.PreparedCall(layers[(rep, depth)], ws, mode, state,
+                                                   required=w.discoveries, eta=w.eta)
+                for rep in range(args.replicas) for depth, mode in enumerate(w.schedule)}
     ev = harness.HipEvents(2 * calls * args.steps)
 
-    def step(i, timed):
+    def step(i, stream, timed=False):
         rep = i % args.replicas
-        for depth, mode in enumerate(w.schedule):
+        for depth in range(len(w.schedule)):
+            pc = prepared[(rep, depth)]
             for layer in range(w.layers):
-                c = depth * w.layers + layer
-                events = harness.EventPair(ev, 2 * (i * calls + c), 2 * (i * calls + c) + 1) if timed else None
-                harness.call(layers[(rep, depth)], ws, mode, state, layer_idx=0,
-                             required=w.discoveries, eta=w.eta, events=events)
+                c = 2 * (i * calls + depth * w.layers + layer)
+                pc.set_events(ev.handle(c), ev.handle(c + 1)) if timed else pc.set_events(None, None)
+                pc.run(stream)
 
+    main_stream = torch.cuda.current_stream()
+    sh = int(main_stream.cuda_stream)
     for i in range(args.warmup):
-        step(i, False)
+        step(i, sh)
     torch.cuda.synchronize()
+
+    # ---- timed region 1 (eager): every split-KV launch bracketed by HIP events ----
     state.counters.zero_()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
     for i in range(args.steps):
-        step(i, True)
+        step(i, sh, timed=True)
     t_end.record()
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    eager_ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ctr = state.counters.cpu().numpy().copy()
+
+    # ---- timed region 2: the same steps replayed from HIP graphs ----
+    graphs = []
+    for rep in range(args.replicas):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(rep, int(torch.cuda.current_stream().cuda_stream))
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % args.replicas].replay()
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        graphs[i % args.replicas].replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
     # ---- per-mode split-kernel times and algorithmic bytes ----
     # the support a sparse depth reads is the one its replica's discovery
     # depths wrote in the same step: rebuild it per replica (untimed)
-    ctr = state.counters.cpu().numpy().copy()
     sup_of = {}
     for rep in range(args.replicas):
-        step(rep, False)
+        step(rep, sh)
         torch.cuda.synchronize()
         sup_of[rep] = state.support_numpy()[:, 0].copy()
     per_mode = {}
@@ -172,11 +195,10 @@ def main():
         m = per_mode.setdefault(key, {"ms": [], "bytes": []})
         nb_of = {rep: split_bytes(w, ctx, mode, sup_of[rep], bt_width) for rep in range(args.replicas)}
         for i in range(args.steps):
-            nbytes = nb_of[i % args.replicas]
             for layer in range(w.layers):
-                c = depth * w.layers + layer
-                m["ms"].append(ev.elapsed_ms(2 * (i * calls + c), 2 * (i * calls + c) + 1))
-                m["bytes"].append(nbytes)
+                c = 2 * (i * calls + depth * w.layers + layer)
+                m["ms"].append(ev.elapsed_ms(c, c + 1))
+                m["bytes"].append(nb_of[i % args.replicas])
     modes_out = {}
     tot_bytes = tot_ms = 0.0
     for key, m in per_mode.items():
@@ -198,12 +220,14 @@ def main():
         "unit": "rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "eager_ms_per_step": round(eager_ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "rows": w.rows, "heads": w.heads, "head_dim": w.head_dim,
                    "ctx": w.ctx if w.ctx else "ragged", "page_size": w.page_size,
                    "layers": w.layers, "schedule": list(w.schedule), "eta": w.eta,
                    "row_calls_per_step": rows_per_step, "kv_replicas": args.replicas,
+                   "timing": "HIP graph replay of whole steps",
                    "union_density": round(float(ctr[W.CTR_SELECTED] / max(1, ctr[W.CTR_CAUSAL])), 4),
                    "fallbacks": int(ctr[W.CTR_FALLBACKS]), "errors": int(ctr[W.CTR_ERRORS])},
         "modes": modes_out,

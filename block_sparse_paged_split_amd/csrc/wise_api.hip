@@ -1,6 +1,7 @@
 // Host entry points of libwise: argument validation, workspace layout, and
 // the launches of the split-KV kernel and the finish kernel on the caller's
 // stream.  Nothing is allocated, nothing is synchronised.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -19,6 +20,7 @@ bool make_layout(int rows, int heads, int head_dim, int max_ctx, Layout *L) {
   if (rows < 1 || heads < 1 || (head_dim != 64 && head_dim != 128)) return false;
   if (max_ctx < 1 || max_ctx > kMaxCtx) return false;
   if (static_cast<int64_t>(rows) * heads > (int64_t{1} << 22)) return false;
+  if (heads > 0x7FFF) return false;  // per-row arrival counts are packed in 16 bits
   L->rows = rows;
   L->heads = heads;
   L->head_dim = head_dim;
@@ -32,8 +34,14 @@ bool make_layout(int rows, int heads, int head_dim, int max_ctx, Layout *L) {
   size_t off = 0;
   L->off_row_code = off;
   off += align256(sizeof(int32_t) * rows);
+  L->off_row_done = off;
+  off += align256(sizeof(unsigned long long) * rows);
   L->off_unit_items = off;
   off += align256(sizeof(int32_t) * units);
+  L->off_n_items = off;
+  off += 256;
+  L->off_item_list = off;
+  off += align256(sizeof(uint32_t) * slots);
   L->off_part_ml = off;
   off += align256(sizeof(float2) * slots);
   L->off_part_acc = off;
@@ -105,6 +113,20 @@ float qk_scale_log2(const wise_attn *a) {
   return static_cast<float>(sc * 1.4426950408889634074);  // log2(e)
 }
 
+// Compute units of the current device (cached per device; the only state
+// the library keeps).
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 int log2i(int x) {
   int s = 0;
   while ((1 << s) < x) ++s;
@@ -162,17 +184,25 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
     p.counters = reinterpret_cast<unsigned long long *>(s->counters);
   }
   p.row_code = reinterpret_cast<int32_t *>(w + L.off_row_code);
+  p.row_done = reinterpret_cast<unsigned long long *>(w + L.off_row_done);
   p.unit_items = reinterpret_cast<int32_t *>(w + L.off_unit_items);
+  p.n_items = reinterpret_cast<int32_t *>(w + L.off_n_items);
+  p.item_list = reinterpret_cast<uint32_t *>(w + L.off_item_list);
   p.part_ml = reinterpret_cast<float2 *>(w + L.off_part_ml);
   p.part_acc = reinterpret_cast<float *>(w + L.off_part_acc);
   p.stats = reinterpret_cast<float2 *>(w + L.off_stats);
   p.stats_export = reinterpret_cast<float2 *>(a->tile_stats);
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
-  if (a->ev_split_begin && hipEventRecord(static_cast<hipEvent_t>(a->ev_split_begin), strm) != hipSuccess)
-    return WISE_E_HIP;
-  if (launch_split(p, a->dtype, a->head_dim, strm) != hipSuccess) return WISE_E_HIP;
-  if (a->ev_split_end && hipEventRecord(static_cast<hipEvent_t>(a->ev_split_end), strm) != hipSuccess)
+  // Rows that may be sparse make item counts data-dependent.  When a unit
+  // spans several split workgroups, plan first and run the persistent split
+  // over the compact item list; otherwise the static grid has one workgroup
+  // per unit and no empty slots worth removing.
+  const bool listed = (row_mode != nullptr || uniform_mode == WISE_SPARSE) && p.chunk_groups > 1;
+  const int cus = listed ? compute_units() : 0;
+  if (listed && cus <= 0) return WISE_E_HIP;
+  if (launch_split(p, a->dtype, a->head_dim, listed, cus, static_cast<hipEvent_t>(a->ev_split_begin),
+                   static_cast<hipEvent_t>(a->ev_split_end), strm) != hipSuccess)
     return WISE_E_HIP;
   return WISE_OK;
 }
@@ -222,6 +252,7 @@ wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *
   p.ctx_len = a->ctx_len;
   p.out = a->out;
   p.row_code = reinterpret_cast<const int32_t *>(w + L.off_row_code);
+  p.row_done = reinterpret_cast<unsigned long long *>(w + L.off_row_done);
   p.unit_items = reinterpret_cast<const int32_t *>(w + L.off_unit_items);
   p.part_ml = reinterpret_cast<const float2 *>(w + L.off_part_ml);
   p.part_acc = reinterpret_cast<const float *>(w + L.off_part_acc);

@@ -9,33 +9,145 @@
 // first discovery depth, its selection and the causal blocks, and for a
 // union depth only the newly set blocks.
 //
-// One 256-thread workgroup per (row, head):
-//  1. merge the unit's items in item order (fixed order, fp32):
-//     M = max m_i, w_i = 2^(m_i - M), L = sum l_i w_i, out = sum acc_i w_i / L;
-//  2. discovery units: block mass p_b = l_b 2^(m_b - M) / L from the tile
-//     stats (fp32), keys (mass descending, block index ascending) sorted by
-//     an LDS bitonic network, running sum in fp64, K = first prefix reaching
-//     eta (at least 1; all blocks if rounding never reaches eta);
-//  3. write (DISCOVER) or OR (DISCOVER_UNION) the unit's support words; add
-//     the density counts; the head-0 workgroup updates the row's tag.
-#include <climits>
-
+// One wave64 per (row, head):
+//  1. merge the unit's items: M = max m_i, w_i = 2^(m_i - M),
+//     L = sum l_i w_i, out = sum acc_i w_i / L (fixed summation orders; the
+//     loads of up to eight items are in flight together);
+//  2. discovery units: block mass p_b = l_b 2^(m_b - M) / L (fp32) from the
+//     tile stats; 64-bit keys (mass bits, ~block index) sorted descending by
+//     a bitonic network held in registers (lane l owns sorted positions
+//     [l*KPL, l*KPL+KPL)); running sum in fp64 (per-lane run, then a wave
+//     scan); K = the first prefix reaching eta, at least 1, all blocks if
+//     rounding never reaches eta;
+//  3. write (DISCOVER) or OR (DISCOVER_UNION) the unit's support words; each
+//     head adds (1 arrival, error flag, selected blocks) to its row's atomic
+//     word, and the last head to arrive updates the row's tag and adds the
+//     row's totals to the density counters (one global atomic per row, not
+//     per head).
 #include "wise_internal.h"
 
 namespace wise {
 
 namespace {
 
-__global__ __launch_bounds__(kFinishThreads) void finish_kernel(const FinishParams p) {
-  extern __shared__ unsigned long long s_keys[];  // [npow] selection keys
-  __shared__ float s_w[kMaxItemsPerUnit];
-  __shared__ float2 s_ml[kMaxItemsPerUnit];
-  __shared__ double s_part[kFinishThreads];
-  __shared__ uint32_t s_bits[kMaxWords];
-  __shared__ float s_M, s_L;
-  __shared__ int s_err, s_K, s_added, s_rowerr;
+constexpr int kLanes = 64;
+constexpr int kUnroll = 8;
 
-  const int tid = threadIdx.x;
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+__device__ __forceinline__ double wave_inclusive_scan(double x, int lane) {
+#pragma unroll
+  for (int d = 1; d < kLanes; d <<= 1) {
+    const double y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), m);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), m);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ float key_mass(unsigned long long key) {
+  return __uint_as_float(static_cast<uint32_t>(key >> 32));
+}
+
+// Selection of one discovery unit with KPL keys per lane (64*KPL >= nb).
+// Returns K; sets the selected blocks' bits in s_bits.
+template <int KPL>
+__device__ __forceinline__ int select_eta(const float2 *st, float eta, int nb, float M, float L, int lane,
+                                          uint32_t *s_bits) {
+  unsigned long long key[KPL];
+  const float invL = 1.0f / L;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int b = lane * KPL + j;
+    key[j] = 0ull;  // padding sorts after every block
+    if (b < nb) {
+      const float2 ml = st[b];
+      const float mass = ml.y * __builtin_amdgcn_exp2f(ml.x - M) * invL;
+      key[j] = (static_cast<unsigned long long>(__float_as_uint(mass)) << 32) |
+               static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(b));
+    }
+  }
+  // bitonic network over positions e = lane*KPL + j, descending keys
+  constexpr int N = kLanes * KPL;
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < KPL) {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          if (j & stride) continue;
+          const int e = lane * KPL + j;
+          const bool desc = (e & size) == 0;
+          const unsigned long long a = key[j], b = key[j | stride];
+          const bool swap = (a < b) == desc;
+          key[j] = swap ? b : a;
+          key[j | stride] = swap ? a : b;
+        }
+      } else {
+        const int lm = stride / KPL;
+        const bool lower = (lane & lm) == 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const int e = lane * KPL + j;
+          const bool desc = (e & size) == 0;
+          const unsigned long long a = key[j], b = shfl_xor64(a, lm);
+          const unsigned long long hi = a > b ? a : b, lo = a > b ? b : a;
+          key[j] = (lower == desc) ? hi : lo;
+        }
+      }
+    }
+  }
+  // fp64 running sum in sorted order
+  double part = 0.0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) part += static_cast<double>(key_mass(key[j]));
+  const double incl = wave_inclusive_scan(part, lane);
+  const double prev = __shfl_up(incl, 1);
+  double run = lane ? prev : 0.0;
+  int kfound = nb;
+  bool hit = false;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    run += static_cast<double>(key_mass(key[j]));
+    if (!hit && run >= static_cast<double>(eta)) {
+      kfound = lane * KPL + j + 1;
+      hit = true;
+    }
+  }
+  const unsigned long long hits = __builtin_amdgcn_ballot_w64(hit);
+  const int K = min(nb, hits ? __builtin_amdgcn_readlane(kfound, __builtin_ctzll(hits)) : nb);
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    if (lane * KPL + j < K) {
+      const uint32_t b = 0xFFFFFFFFu - static_cast<uint32_t>(key[j]);
+      atomicOr(&s_bits[b >> 5], 1u << (b & 31));
+    }
+  }
+  return K;
+}
+
+__global__ __launch_bounds__(kLanes) void finish_kernel(const FinishParams p) {
+  __shared__ float s_w[kMaxItemsPerUnit];
+  __shared__ uint32_t s_bits[kMaxWords];
+
+  const int lane = threadIdx.x;
   const int u = blockIdx.x;
   const int r = u / p.heads;
   const int h = u - r * p.heads;
@@ -48,114 +160,92 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(const FinishPara
   const int D = p.head_dim;
 
   // ---- 1. merge ----
-  for (int i = tid; i < items; i += kFinishThreads) s_ml[i] = p.part_ml[base + i];
-  __syncthreads();
-  if (tid == 0) {
-    float M = -INFINITY;
-    int err = items == 0;
-    for (int i = 0; i < items; ++i) {
-      err |= s_ml[i].y < 0.0f;
-      M = fmaxf(M, s_ml[i].x);
-    }
-    float L = 0.0f;
-    for (int i = 0; i < items; ++i) {
-      const float w = __builtin_amdgcn_exp2f(s_ml[i].x - M);
-      s_w[i] = w;
-      L = fmaf(s_ml[i].y, w, L);
-    }
-    s_M = M;
-    s_L = L;
-    s_err = err;
-    s_K = INT_MAX;
-    s_added = 0;
-    s_rowerr = 0;
+  // The accumulators of the first kUnroll items do not depend on the merge
+  // weights: their loads go out first, together with the (m, l) loads.
+  constexpr int kDims = 2;  // head_dim <= 2 * 64
+  const float *acc = p.part_acc + base * D;
+  float v[kDims][kUnroll];
+#pragma unroll
+  for (int q = 0; q < kDims; ++q) {
+    const int dd = lane + q * kLanes;
+#pragma unroll
+    for (int t = 0; t < kUnroll; ++t) v[q][t] = (dd < D && t < items) ? acc[t * D + dd] : 0.0f;
   }
+  float2 ml_own[kMaxItemsPerUnit / kLanes];
+  float M = -INFINITY;
+  bool bad_item = false;
+#pragma unroll
+  for (int c = 0; c < kMaxItemsPerUnit / kLanes; ++c) {
+    const int i = c * kLanes + lane;
+    ml_own[c] = i < items ? p.part_ml[base + i] : make_float2(-INFINITY, 0.0f);
+    bad_item |= ml_own[c].y < 0.0f;
+    M = fmaxf(M, ml_own[c].x);
+  }
+  M = wave_max(M);
+  const bool err = items == 0 || __builtin_amdgcn_ballot_w64(bad_item) != 0ull;
+  float Lp = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMaxItemsPerUnit / kLanes; ++c) {
+    const int i = c * kLanes + lane;
+    if (i < items) {
+      const float w = __builtin_amdgcn_exp2f(ml_own[c].x - M);
+      s_w[i] = w;
+      Lp = fmaf(ml_own[c].y, w, Lp);
+    }
+  }
+  const float L = wave_sum(Lp);
   __syncthreads();
-  const float M = s_M, L = s_L;
-  const bool err = s_err != 0;
-  for (int dd = tid; dd < D; dd += kFinishThreads) {
+#pragma unroll
+  for (int q = 0; q < kDims; ++q) {
+    const int dd = lane + q * kLanes;
+    if (dd >= D) break;
     float a = 0.0f;
-    for (int i = 0; i < items; ++i) a = fmaf(p.part_acc[(base + i) * D + dd], s_w[i], a);
+#pragma unroll
+    for (int t = 0; t < kUnroll; ++t)
+      if (t < items) a = fmaf(v[q][t], s_w[t], a);
+    for (int i0 = kUnroll; i0 < items; i0 += kUnroll) {
+      float x[kUnroll];
+#pragma unroll
+      for (int t = 0; t < kUnroll; ++t) x[t] = i0 + t < items ? acc[(i0 + t) * D + dd] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < kUnroll; ++t)
+        if (i0 + t < items) a = fmaf(x[t], s_w[i0 + t], a);
+    }
     p.out[static_cast<int64_t>(u) * D + dd] = err ? __builtin_nanf("") : a / L;
   }
-  if (err && tid == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
+  if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
 
   if (p.support == nullptr || row_bad || req == WISE_DENSE) return;
   const int slot = p.slot_of_row ? p.slot_of_row[r] : r;
-
-  // ---- 2. eta selection of a discovery unit ----
   const bool discover = eff == WISE_DISCOVER || eff == WISE_DISCOVER_UNION;
-  if (discover && !err) {
-    const int nb = (p.ctx_len[r] + kBlock - 1) / kBlock;
-    int npow = 1;
-    while (npow < nb) npow <<= 1;
-    const float invL = 1.0f / L;
-    for (int b = tid; b < npow; b += kFinishThreads) {
-      unsigned long long key = 0ull;  // padding sorts after every block
-      if (b < nb) {
-        const float2 st = p.stats[static_cast<int64_t>(u) * p.max_blocks + b];
-        const float mass = st.y * __builtin_amdgcn_exp2f(st.x - M) * invL;
-        key = (static_cast<unsigned long long>(__float_as_uint(mass)) << 32) |
-              static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(b));
-      }
-      s_keys[b] = key;
-    }
-    for (int w = tid; w < kMaxWords; w += kFinishThreads) s_bits[w] = 0u;
-    __syncthreads();
-    // bitonic sort, descending keys: mass descending, then block index ascending
-    for (int size = 2; size <= npow; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int t = tid; t < (npow >> 1); t += kFinishThreads) {
-          const int lo = 2 * stride * (t / stride) + (t % stride);
-          const int hi = lo + stride;
-          const bool desc = (lo & size) == 0;
-          const unsigned long long a = s_keys[lo], bkey = s_keys[hi];
-          if ((a < bkey) == desc) {
-            s_keys[lo] = bkey;
-            s_keys[hi] = a;
-          }
-        }
-        __syncthreads();
-      }
-    }
-    // running sum in fp64: each thread owns a contiguous run of the order
-    const int per = (nb + kFinishThreads - 1) / kFinishThreads;
-    const int lo = min(nb, tid * per), hi = min(nb, lo + per);
-    double sum = 0.0;
-    for (int i = lo; i < hi; ++i) sum += static_cast<double>(__uint_as_float(static_cast<uint32_t>(s_keys[i] >> 32)));
-    s_part[tid] = sum;
-    __syncthreads();
-    if (tid == 0) {
-      double run = 0.0;
-      for (int t = 0; t < kFinishThreads; ++t) {
-        const double x = s_part[t];
-        s_part[t] = run;
-        run += x;
-      }
-    }
-    __syncthreads();
-    double run = s_part[tid];
-    int kfound = INT_MAX;
-    for (int i = lo; i < hi; ++i) {
-      run += static_cast<double>(__uint_as_float(static_cast<uint32_t>(s_keys[i] >> 32)));
-      if (run >= static_cast<double>(p.eta)) {
-        kfound = i + 1;
-        break;
-      }
-    }
-    if (kfound != INT_MAX) atomicMin(&s_K, kfound);
-    __syncthreads();
-    const int K = s_K == INT_MAX ? nb : max(1, s_K);
-    for (int i = tid; i < K; i += kFinishThreads) {
-      const uint32_t b = 0xFFFFFFFFu - static_cast<uint32_t>(s_keys[i]);
-      atomicOr(&s_bits[b >> 5], 1u << (b & 31));
-    }
-    __syncthreads();
+  wise_tag *tag = p.tags + static_cast<int64_t>(slot) * p.layers + p.layer;
 
-    // ---- 3. support write / union, density counts ----
+  if (!discover) {
+    // a union row whose discovery window is broken ran dense: the rest of
+    // this token runs dense too
+    if (req == WISE_DISCOVER_UNION && h == 0 && lane == 0) tag->discoveries = 0;
+    return;
+  }
+
+  // ---- 2. eta selection, 3. support write / union ----
+  const int nb = (p.ctx_len[r] + kBlock - 1) / kBlock;
+  int selected = 0;
+  if (!err) {
+    for (int w = lane; w < kMaxWords; w += kLanes) s_bits[w] = 0u;
+    __syncthreads();
+    const float2 *st = p.stats + static_cast<int64_t>(u) * p.max_blocks;
+    const float eta = p.eta;
+    int K;
+    if (nb <= kLanes) K = select_eta<1>(st, eta, nb, M, L, lane, s_bits);
+    else if (nb <= 2 * kLanes) K = select_eta<2>(st, eta, nb, M, L, lane, s_bits);
+    else if (nb <= 4 * kLanes) K = select_eta<4>(st, eta, nb, M, L, lane, s_bits);
+    else if (nb <= 8 * kLanes) K = select_eta<8>(st, eta, nb, M, L, lane, s_bits);
+    else if (nb <= 16 * kLanes) K = select_eta<16>(st, eta, nb, M, L, lane, s_bits);
+    else K = select_eta<32>(st, eta, nb, M, L, lane, s_bits);
+    __syncthreads();
     uint32_t *sw = p.support + ((static_cast<int64_t>(slot) * p.layers + p.layer) * p.heads + h) * p.words;
     int added = 0;
-    for (int w = tid; w < p.words; w += kFinishThreads) {
+    for (int w = lane; w < p.words; w += kLanes) {
       const uint32_t nw = w < kMaxWords ? s_bits[w] : 0u;
       if (eff == WISE_DISCOVER) {
         sw[w] = nw;
@@ -165,49 +255,35 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(const FinishPara
         added += __popc(nw & ~old);
       }
     }
-    if (added) atomicAdd(&s_added, added);
-    __syncthreads();
-    if (tid == 0 && p.counters) {
-      atomicAdd(p.counters + WISE_CTR_SELECTED,
-                static_cast<unsigned long long>(eff == WISE_DISCOVER ? K : s_added));
-      if (eff == WISE_DISCOVER) atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(nb));
-    }
+    selected = eff == WISE_DISCOVER ? K : wave_sum_int(added);
   }
 
-  // ---- tag of the row's (slot, layer), once per row ----
-  if (h != 0) return;
-  if (discover) {
-    // a bad page in any head of the row breaks this discovery
-    for (int hh = 0; hh < p.heads; ++hh) {
-      const int uu = r * p.heads + hh;
-      const int it = p.unit_items[uu];
-      const int64_t bb = static_cast<int64_t>(uu) * p.items_per_unit;
-      for (int i = tid; i < it; i += kFinishThreads)
-        if (p.part_ml[bb + i].y < 0.0f) s_rowerr = 1;
-    }
-    __syncthreads();
+  // ---- the row's tag and density counts: by the last of its heads to arrive ----
+  if (lane != 0) return;
+  const unsigned long long mine =
+      1ull | (err ? (1ull << 16) : 0ull) | (static_cast<unsigned long long>(selected) << 32);
+  const unsigned long long all = atomicAdd(p.row_done + r, mine) + mine;
+  if (static_cast<int>(all & 0xFFFFull) != p.heads) return;
+  const int err_heads = static_cast<int>((all >> 16) & 0xFFFFull);
+  if (p.counters) {
+    atomicAdd(p.counters + WISE_CTR_SELECTED, all >> 32);
+    if (eff == WISE_DISCOVER)
+      atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(nb) * (p.heads - err_heads));
   }
-  if (tid != 0) return;
-  wise_tag *t = p.tags + static_cast<int64_t>(slot) * p.layers + p.layer;
+  // a bad page in any head of the row breaks this discovery
   if (eff == WISE_DISCOVER) {
-    t->request = p.row_request[r];
-    t->position = p.row_position[r];
-    t->discoveries = s_rowerr ? 0 : 1;
-  } else if (eff == WISE_DISCOVER_UNION) {
-    t->discoveries = s_rowerr ? 0 : t->discoveries + 1;
-  } else if (req == WISE_DISCOVER_UNION) {
-    t->discoveries = 0;  // broken window: the rest of this token runs dense
+    tag->request = p.row_request[r];
+    tag->position = p.row_position[r];
+    tag->discoveries = err_heads ? 0 : 1;
+  } else {
+    tag->discoveries = err_heads ? 0 : tag->discoveries + 1;
   }
 }
 
 }  // namespace
 
 hipError_t launch_finish(const FinishParams &p, hipStream_t stream) {
-  int npow = 1;
-  while (npow < p.max_blocks) npow <<= 1;
-  const size_t lds = static_cast<size_t>(npow) * sizeof(unsigned long long);
-  hipLaunchKernelGGL(finish_kernel, dim3(static_cast<unsigned>(p.rows) * p.heads), dim3(kFinishThreads), lds,
-                     stream, p);
+  hipLaunchKernelGGL(finish_kernel, dim3(static_cast<unsigned>(p.rows) * p.heads), dim3(kLanes), 0, stream, p);
   return hipGetLastError();
 }
 

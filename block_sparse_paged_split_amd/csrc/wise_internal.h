@@ -16,9 +16,9 @@ constexpr int kMaxTilesPerItem = 16;   // upper bound of tiles per work item
 constexpr int kMaxCtx = 65536;         // tokens; 2048 blocks, 64 support words
 constexpr int kMaxBlocks = kMaxCtx / kBlock;
 constexpr int kMaxWords = kMaxBlocks / 32;
-constexpr int kFinishThreads = 256;
 constexpr int kMaxItemsPerUnit = 512;  // kMaxBlocks / smallest tiles-per-item (4)
 constexpr int kRowError = 0xF;         // row code: bad device data for the row
+constexpr int kItemBits = 9;           // item list entry: unit << 9 | item (kMaxItemsPerUnit = 2^9)
 
 // Row code written by the split kernel (wave of head 0, item 0) and read by
 // the finish kernel: effective mode in bits 0..3 (kRowError for a bad row),
@@ -32,7 +32,8 @@ int tiles_per_item(int max_blocks);
 
 struct Layout {
   int rows, heads, head_dim, max_ctx, max_blocks, tiles_per_item, items_per_unit;
-  size_t off_row_code, off_unit_items, off_part_ml, off_part_acc, off_stats, total;
+  size_t off_row_code, off_row_done, off_unit_items, off_n_items, off_item_list, off_part_ml, off_part_acc,
+      off_stats, total;
 };
 // Returns false if the sizes are outside the supported range.
 bool make_layout(int rows, int heads, int head_dim, int max_ctx, Layout *L);
@@ -58,6 +59,9 @@ struct SplitParams {
   unsigned long long *counters;
   // workspace and optional export
   int32_t *row_code, *unit_items;
+  unsigned long long *row_done;
+  int32_t *n_items;      // live items in item_list (calls with sparse rows)
+  uint32_t *item_list;   // unit << kItemBits | item
   float2 *part_ml;
   float *part_acc;
   float2 *stats;
@@ -69,6 +73,9 @@ struct FinishParams {
   const int32_t *ctx_len;
   float *out;
   const int32_t *row_code, *unit_items;
+  // per row, one atomic word: heads finished (bits 0..15), heads with an
+  // error (bits 16..31), blocks newly selected by the row's heads (32..63)
+  unsigned long long *row_done;
   const float2 *part_ml;
   const float *part_acc;
   const float2 *stats;
@@ -82,7 +89,12 @@ struct FinishParams {
   unsigned long long *counters;
 };
 
-hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, hipStream_t stream);
+// listed = plan kernel + persistent split over the compact item list (calls
+// with sparse rows); otherwise the static one-wave-per-item-slot grid.
+// cus = compute units of the current device (sizes the persistent grid);
+// ev_begin / ev_end (optional) are recorded right around the split kernel.
+hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, int cus, hipEvent_t ev_begin,
+                        hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_finish(const FinishParams &p, hipStream_t stream);
 
 }  // namespace wise

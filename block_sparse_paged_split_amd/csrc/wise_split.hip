@@ -23,6 +23,8 @@
 //    runs in base 2 on scores pre-scaled by scale*log2(e).  Every reduction
 //    is a fixed butterfly, so all lanes hold bitwise-identical statistics and
 //    a row's result does not depend on the other rows of the launch.
+#include <algorithm>
+
 #include "wise_internal.h"
 
 namespace wise {
@@ -39,6 +41,8 @@ struct Geo {
   static constexpr int TPI = 64 / LPT;          // tokens per load instruction
   static constexpr int NI = kBlock / TPI;       // load instructions per tile
   static constexpr int EPL = 16 / E;            // elements per lane per load
+  // waves per SIMD the persistent split kernel is compiled for (VGPR budget)
+  static constexpr int kListedWavesPerEU = NI * 8 <= 64 ? 4 : 2;
   static_assert(LPT >= 8 && LPT <= 32, "unsupported head_dim/dtype");
 };
 
@@ -140,74 +144,77 @@ __device__ __forceinline__ u32x4 load16(const char *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
-template <bool kBf16, int D>
-__global__ __launch_bounds__(64 * kWavesPerGroup) void split_kernel(const SplitParams p) {
-  using G = Geo<kBf16, D>;
-  __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
+// ---------------------------------------------------------------------------
+// Planning of one row: effective mode from the support tags, dense fallback.
+// ---------------------------------------------------------------------------
+struct RowPlan {
+  int n, req, eff, slot;
+  bool bad, fallback;
+};
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u = blockIdx.x / p.chunk_groups;                         // unit = (row, head)
-  const int k = (blockIdx.x - u * p.chunk_groups) * kWavesPerGroup + wave;  // item slot
-  if (k >= p.items_per_unit) return;
-  const int r = u / p.heads;
-  const int h = u - r * p.heads;
-
-  // ---- plan: effective mode of the row (support tags), dense fallback ----
-  const int n = p.ctx_len[r];
-  const int req = p.row_mode ? static_cast<int>(p.row_mode[r]) : p.uniform_mode;
-  bool bad = n < 1 || n > p.max_ctx || req < WISE_DENSE || req > WISE_SPARSE;
-  int eff = req, slot = r;
-  bool fallback = false;
-  if (!bad && req != WISE_DENSE) {
-    if (p.slot_of_row) slot = p.slot_of_row[r];
-    if (slot < 0 || slot >= p.slots) {
-      bad = true;
-    } else if (req == WISE_DISCOVER_UNION || req == WISE_SPARSE) {
-      const wise_tag *t = p.tags + static_cast<int64_t>(slot) * p.layers + p.layer;
+__device__ __forceinline__ RowPlan plan_row(const SplitParams &p, int r) {
+  RowPlan rp;
+  rp.n = p.ctx_len[r];
+  rp.req = p.row_mode ? static_cast<int>(p.row_mode[r]) : p.uniform_mode;
+  rp.bad = rp.n < 1 || rp.n > p.max_ctx || rp.req < WISE_DENSE || rp.req > WISE_SPARSE;
+  rp.eff = rp.req;
+  rp.slot = r;
+  rp.fallback = false;
+  if (!rp.bad && rp.req != WISE_DENSE) {
+    if (p.slot_of_row) rp.slot = p.slot_of_row[r];
+    if (rp.slot < 0 || rp.slot >= p.slots) {
+      rp.bad = true;
+    } else if (rp.req == WISE_DISCOVER_UNION || rp.req == WISE_SPARSE) {
+      const wise_tag *t = p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer;
       const bool same = t->request == p.row_request[r] && t->position == p.row_position[r];
-      const int need = req == WISE_SPARSE ? p.required : 1;
+      const int need = rp.req == WISE_SPARSE ? p.required : 1;
       if (!(same && t->discoveries >= need)) {
-        eff = WISE_DENSE;
-        fallback = true;
+        rp.eff = WISE_DENSE;
+        rp.fallback = true;
       }
     }
   }
+  return rp;
+}
 
-  // ---- tile count: all causal tiles, or the support's set bits ----
-  const int nb = bad ? 0 : (n + kBlock - 1) / kBlock;
-  const bool sparse = !bad && eff == WISE_SPARSE;
-  int count = nb;
-  uint32_t word = 0;
-  int incl = 0;
-  if (sparse) {
-    const uint32_t *sw =
-        p.support + ((static_cast<int64_t>(slot) * p.layers + p.layer) * p.heads + h) * p.words;
-    const int nw = (nb + 31) >> 5;
-    if (lane < nw) {
-      word = sw[lane];
-      const int valid = nb - 32 * lane;
-      if (valid < 32) word &= (1u << valid) - 1u;
-    }
-    incl = wave_inclusive_scan(__popc(word), lane);
-    count = __builtin_amdgcn_readlane(incl, 63);
+__device__ __forceinline__ const uint32_t *support_words(const SplitParams &p, int slot, int h) {
+  return p.support + ((static_cast<int64_t>(slot) * p.layers + p.layer) * p.heads + h) * p.words;
+}
+
+// One wave: lane l < ceil(nb/32) holds support word l (bits past nb cleared);
+// incl = inclusive prefix of the words' popcounts; returns the set-bit count.
+__device__ __forceinline__ int support_scan(const SplitParams &p, int slot, int h, int nb, int lane,
+                                            uint32_t &word, int &incl) {
+  const uint32_t *sw = support_words(p, slot, h);
+  const int nw = (nb + 31) >> 5;
+  word = 0u;
+  if (lane < nw) {
+    word = sw[lane];
+    const int valid = nb - 32 * lane;
+    if (valid < 32) word &= (1u << valid) - 1u;
   }
+  incl = wave_inclusive_scan(__popc(word), lane);
+  return __builtin_amdgcn_readlane(incl, 63);
+}
+
+// ---------------------------------------------------------------------------
+// One work item: list entries [first, first + ntiles) of unit (r, h) --
+// either tiles first.. (all causal tiles) or the support's set bits of those
+// ranks, compacted into a per-wave list before the loop.  Writes the
+// item's partial (m, l, acc) and the tile stats.
+// ---------------------------------------------------------------------------
+template <bool kBf16, int D>
+__device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int h, int k, int n, bool sparse,
+                                         int count, uint32_t word, int incl, int lane, int *tiles) {
+  using G = Geo<kBf16, D>;
   const int T = p.tiles_per_item;
-  const int items = bad ? 0 : (count + T - 1) / T;
-  if (k == 0 && lane == 0) {
-    p.unit_items[u] = items;
-    if (h == 0) {
-      p.row_code[r] = encode_row(bad ? kRowError : eff, req);
-      if (fallback && p.counters) atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
-    }
-  }
-  if (k >= items) return;
-
   const int first = k * T;
   const int ntiles = min(T, count - first);
 
-  // ---- compact this item's slice of the support into a tile list ----
   if (sparse) {
+    // the previous item of this wave may still be reading the list
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
     const int excl = incl - __popc(word);
     const unsigned long long past = __builtin_amdgcn_ballot_w64(incl > first);
     int w = __builtin_amdgcn_readfirstlane(__builtin_ctzll(past));
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_kernel(const SplitP
       const unsigned long long bm = __builtin_amdgcn_ballot_w64(set);
       const int rank = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
                                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0));
-      if (set && rank >= first && rank < first + ntiles) s_tiles[wave][rank - first] = 32 * w + lane;
+      if (set && rank >= first && rank < first + ntiles) tiles[rank - first] = 32 * w + lane;
       got = min(ntiles, base + __popcll(bm) - first);
       ++w;
     }
@@ -251,9 +258,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_kernel(const SplitP
   // all past the context reuses the page of the row's last token with the
   // slot offset it would have had, which stays inside that page; its lanes
   // are masked below.
-  auto tile_of = [&](int i) -> int {
-    return sparse ? __builtin_amdgcn_readfirstlane(s_tiles[wave][i]) : first + i;
-  };
+  auto tile_of = [&](int i) -> int { return sparse ? __builtin_amdgcn_readfirstlane(tiles[i]) : first + i; };
   auto fetch_pages = [&](int b) -> int {
     const int tj = b * kBlock + min(lane, G::NI - 1) * G::TPI;
     return bt[min(tj, n - 1) >> p.page_shift];
@@ -332,30 +337,185 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_kernel(const SplitP
   }
   if (lane == 0) p.part_ml[slot_idx] = page_err ? make_float2(0.0f, -1.0f) : make_float2(m_run, l_run);
   if (lane < ntiles) {
-    const int b = sparse ? s_tiles[wave][lane] : first + lane;
+    const int b = sparse ? tiles[lane] : first + lane;
     const int64_t si = static_cast<int64_t>(u) * p.max_blocks + b;
     p.stats[si] = make_float2(st_m, st_l);
     if (p.stats_export) p.stats_export[si] = make_float2(st_m * kLn2, st_l);
   }
 }
 
+// ---------------------------------------------------------------------------
+// Static grid: one wave per (unit, item slot); every wave plans its own item.
+// Used when no row is sparse, so every unit's item count is known from its
+// context length and (nearly) every slot holds work.
+// ---------------------------------------------------------------------------
+template <bool kBf16, int D>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const SplitParams p) {
+  __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u = blockIdx.x / p.chunk_groups;                                // unit = (row, head)
+  const int k = (blockIdx.x - u * p.chunk_groups) * kWavesPerGroup + wave;  // item slot
+  if (k >= p.items_per_unit) return;
+  const int r = u / p.heads;
+  const int h = u - r * p.heads;
+  const RowPlan rp = plan_row(p, r);
+  const int nb = rp.bad ? 0 : (rp.n + kBlock - 1) / kBlock;
+  const bool sparse = !rp.bad && rp.eff == WISE_SPARSE;
+  uint32_t word = 0u;
+  int incl = 0;
+  const int count = sparse ? support_scan(p, rp.slot, h, nb, lane, word, incl) : nb;
+  const int items = (count + p.tiles_per_item - 1) / p.tiles_per_item;
+  if (k == 0 && lane == 0) {
+    p.unit_items[u] = items;
+    if (h == 0) {
+      p.row_code[r] = encode_row(rp.bad ? kRowError : rp.eff, rp.req);
+      p.row_done[r] = 0ull;  // the finish kernel's per-row arrival word
+      if (rp.fallback && p.counters) atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
+    }
+  }
+  if (k >= items) return;
+  run_item<kBf16, D>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave]);
+}
+
+// ---------------------------------------------------------------------------
+// Plan kernel (one workgroup) for calls with sparse rows: effective modes,
+// per-unit item counts, and the compact list of live items, so that the
+// split grid carries no empty item slots.
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const SplitParams p) {
+  __shared__ int s_scan[kPlanThreads];
+  const int t = threadIdx.x;
+  const int U = p.rows * p.heads;
+  const int per = (U + kPlanThreads - 1) / kPlanThreads;
+  const int u0 = min(U, t * per), u1 = min(U, u0 + per);
+  int local = 0;
+  for (int u = u0; u < u1; ++u) {
+    const int r = u / p.heads;
+    const int h = u - r * p.heads;
+    const RowPlan rp = plan_row(p, r);
+    const int nb = rp.bad ? 0 : (rp.n + kBlock - 1) / kBlock;
+    int count = nb;
+    if (!rp.bad && rp.eff == WISE_SPARSE) {
+      const uint32_t *sw = support_words(p, rp.slot, h);
+      count = 0;
+      for (int w = 0; 32 * w < nb; ++w) {
+        uint32_t x = sw[w];
+        const int valid = nb - 32 * w;
+        if (valid < 32) x &= (1u << valid) - 1u;
+        count += __popc(x);
+      }
+    }
+    const int items = (count + p.tiles_per_item - 1) / p.tiles_per_item;
+    p.unit_items[u] = items;
+    local += items;
+    if (h == 0) {
+      p.row_code[r] = encode_row(rp.bad ? kRowError : rp.eff, rp.req);
+      p.row_done[r] = 0ull;
+      if (rp.fallback && p.counters) atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
+    }
+  }
+  // exclusive scan of the per-thread item counts (Hillis-Steele in LDS)
+  s_scan[t] = local;
+  __syncthreads();
+  for (int d = 1; d < kPlanThreads; d <<= 1) {
+    const int y = t >= d ? s_scan[t - d] : 0;
+    __syncthreads();
+    s_scan[t] += y;
+    __syncthreads();
+  }
+  int at = s_scan[t] - local;
+  for (int u = u0; u < u1; ++u) {
+    const int items = p.unit_items[u];
+    for (int kk = 0; kk < items; ++kk) p.item_list[at + kk] = (static_cast<uint32_t>(u) << kItemBits) | kk;
+    at += items;
+  }
+  if (t == kPlanThreads - 1) *p.n_items = s_scan[t];
+}
+
+// ---------------------------------------------------------------------------
+// Listed grid: persistent waves striding over the compact item list.
+// ---------------------------------------------------------------------------
+template <bool kBf16, int D>
+__global__ __launch_bounds__(64 * kWavesPerGroup) __attribute__((amdgpu_waves_per_eu(Geo<kBf16, D>::kListedWavesPerEU)))
+void split_listed_kernel(const SplitParams p) {
+  __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int stride = gridDim.x * kWavesPerGroup;
+  const int n_items = *p.n_items;
+  for (int i = blockIdx.x * kWavesPerGroup + wave; i < n_items; i += stride) {
+    const uint32_t it = p.item_list[i];
+    const int u = static_cast<int>(it >> kItemBits);
+    const int k = static_cast<int>(it & ((1u << kItemBits) - 1u));
+    const int r = u / p.heads;
+    const int h = u - r * p.heads;
+    const int n = p.ctx_len[r];
+    const int eff = p.row_code[r] & 0xF;
+    const bool sparse = eff == WISE_SPARSE;
+    int slot = r;
+    if (sparse && p.slot_of_row) slot = p.slot_of_row[r];
+    uint32_t word = 0u;
+    int incl = 0;
+    const int nb = (n + kBlock - 1) / kBlock;
+    const int count = sparse ? support_scan(p, slot, h, nb, lane, word, incl) : nb;
+    run_item<kBf16, D>(p, u, r, h, k, n, sparse, count, word, incl, lane, s_tiles[wave]);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
-  const dim3 block(64 * kWavesPerGroup);
-  if (dtype == WISE_BF16 && head_dim == 128) {
-    hipLaunchKernelGGL((split_kernel<true, 128>), grid, block, 0, stream, p);
-  } else if (dtype == WISE_BF16 && head_dim == 64) {
-    hipLaunchKernelGGL((split_kernel<true, 64>), grid, block, 0, stream, p);
-  } else if (dtype == WISE_F32 && head_dim == 128) {
-    hipLaunchKernelGGL((split_kernel<false, 128>), grid, block, 0, stream, p);
-  } else if (dtype == WISE_F32 && head_dim == 64) {
-    hipLaunchKernelGGL((split_kernel<false, 64>), grid, block, 0, stream, p);
-  } else {
-    return hipErrorInvalidValue;
+// Resident workgroups of the listed split kernel on one CU of the current
+// device (occupancy query, cached per device and instantiation).
+template <bool kBf16, int D>
+static int listed_groups_per_cu() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_listed_kernel<kBf16, D>, 64 * kWavesPerGroup, 0) !=
+            hipSuccess ||
+        n < 1)
+      return -1;
+    cache[dev] = n;
   }
-  return hipGetLastError();
+  return cache[dev];
+}
+
+template <bool kBf16, int D>
+static hipError_t launch_typed(const SplitParams &p, bool listed, int cus, hipEvent_t ev_begin, hipEvent_t ev_end,
+                               hipStream_t stream) {
+  const dim3 block(64 * kWavesPerGroup);
+  if (listed) {
+    const int per_cu = listed_groups_per_cu<kBf16, D>();
+    if (per_cu < 1) return hipErrorInvalidValue;
+    const int64_t slot_groups =
+        (static_cast<int64_t>(p.rows) * p.heads * p.items_per_unit + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int groups = static_cast<int>(std::min<int64_t>(slot_groups, static_cast<int64_t>(cus) * per_cu));
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((split_listed_kernel<kBf16, D>), dim3(groups), block, 0, stream, p);
+  } else {
+    const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
+    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((split_static_kernel<kBf16, D>), grid, block, 0, stream, p);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, int cus, hipEvent_t ev_begin,
+                        hipEvent_t ev_end, hipStream_t stream) {
+  if (dtype == WISE_BF16 && head_dim == 128) return launch_typed<true, 128>(p, listed, cus, ev_begin, ev_end, stream);
+  if (dtype == WISE_BF16 && head_dim == 64) return launch_typed<true, 64>(p, listed, cus, ev_begin, ev_end, stream);
+  if (dtype == WISE_F32 && head_dim == 128) return launch_typed<false, 128>(p, listed, cus, ev_begin, ev_end, stream);
+  if (dtype == WISE_F32 && head_dim == 64) return launch_typed<false, 64>(p, listed, cus, ev_begin, ev_end, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace wise

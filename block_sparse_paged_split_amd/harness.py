@@ -141,6 +141,42 @@ def call(layer: DeviceLayer, ws: Workspace, mode: int, state: Optional[SupportSt
     W.wise_finish_select(a, s, ws.ptr, ws.nbytes, st)
 
 
+class PreparedCall:
+    """One (depth, layer) call with its ctypes arguments built once, so that
+    issuing it costs two foreign calls (decode, finish)."""
+
+    def __init__(self, layer: DeviceLayer, ws: Workspace, mode: int,
+                 state: Optional[SupportState] = None, layer_idx: int = 0, required: int = 2,
+                 eta: float = 0.95, row_mode=None):
+        self.a = layer.attn()
+        self.s = state.view(layer_idx, required, eta) if state is not None else None
+        self.mode = mode
+        self.row_mode = None if row_mode is None else int(row_mode.data_ptr())
+        self.ws, self.nbytes = ws.ptr, ws.nbytes
+        self.L = W.lib()
+        self.pa = ctypes.byref(self.a)
+        self.ps = None if self.s is None else ctypes.byref(self.s)
+
+    def set_events(self, begin: Optional[int], end: Optional[int]) -> None:
+        self.a.ev_split_begin = begin
+        self.a.ev_split_end = end
+
+    def run(self, stream: int) -> None:
+        L, m = self.L, self.mode
+        if self.row_mode is not None or m == W.WISE_SPARSE:
+            st = L.wise_decode_sparse(self.pa, self.ps, self.row_mode, self.ws, self.nbytes, stream)
+        elif m == W.WISE_DENSE:
+            st = L.wise_decode_dense(self.pa, self.ws, self.nbytes, stream)
+        else:
+            st = L.wise_decode_discover(self.pa, self.ps, int(m == W.WISE_DISCOVER_UNION), self.ws,
+                                        self.nbytes, stream)
+        if st != W.WISE_OK:
+            raise W.WiseError(st, "decode")
+        st = L.wise_finish_select(self.pa, self.ps, self.ws, self.nbytes, stream)
+        if st != W.WISE_OK:
+            raise W.WiseError(st, "finish")
+
+
 class HipEvents:
     """Raw HIP events (hipEventCreate) usable as the library's timing hook."""
 

@@ -76,11 +76,13 @@ def _one_layer(w, depth=0):
     return li, harness.upload(li, with_stats=True)
 
 
-def test_modes_agree_bitwise(torch):
+@pytest.mark.parametrize("ctx,rows", [(1024, 32), (4096, 8)])
+def test_modes_agree_bitwise(torch, ctx, rows):
     """discover output == dense output; sparse with every block == dense;
-    reruns are bitwise identical."""
-    w = synth.WORKLOADS["ctx1k"]
-    say("[ctx1k] dense / discover / all-blocks sparse, bitwise")
+    reruns are bitwise identical.  At 4K the sparse call runs the planned
+    (listed) split and the dense call the static one."""
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], ctx=ctx, rows=rows, name=f"modes{ctx}")
+    say(f"[{w.name}] dense / discover / all-blocks sparse, bitwise")
     li, dev = _one_layer(w)
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
     harness.call(dev, ws, W.WISE_DENSE)
@@ -103,9 +105,10 @@ def test_modes_agree_bitwise(torch):
     assert state.counters[W.CTR_FALLBACKS].item() == 0
 
 
-def test_mixed_launch_equals_uniform(torch):
-    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=16, name="mixed16")
-    say("[mixed16] one mixed launch vs uniform launches")
+@pytest.mark.parametrize("ctx", [1024, 4096])
+def test_mixed_launch_equals_uniform(torch, ctx):
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=16, ctx=ctx, name=f"mixed16_{ctx}")
+    say(f"[{w.name}] one mixed launch vs uniform launches")
     li0, dev0 = _one_layer(w, 0)
     li1, dev1 = _one_layer(w, 1)
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
@@ -139,7 +142,7 @@ def test_mixed_launch_equals_uniform(torch):
 
 # ----------------------------------------------------------------------------- ragged and layouts
 
-RAGGED = (1, 2, 31, 32, 33, 63, 64, 65, 100, 257, 1000)
+RAGGED = (1, 2, 31, 32, 33, 63, 64, 65, 100, 257, 1000, 2900)  # 2900: units span several split groups
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
@@ -238,3 +241,37 @@ def test_device_data_errors(torch):
     assert np.isnan(out[[0, 2, 4]]).all() and np.isnan(out[5, 1]).all()
     assert not np.isnan(out[3]).any() and not np.isnan(out[5, 0]).any()
     # row 1's bad page sits in block 1: NaN only for heads whose support holds it
+
+
+def test_graph_replay_matches_eager(torch):
+    """A whole step captured in a HIP graph: every replay (with eager work and
+    synchronisation in between) equals the eager step bit for bit."""
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=8, name="graph8")
+    say("[graph8] capture one step (4 depths), replay x3")
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    devs = [harness.upload(synth.layer_inputs(w, d)) for d in range(len(w.schedule))]
+    calls = [harness.PreparedCall(devs[d], ws, m, st, required=w.discoveries, eta=w.eta)
+             for d, m in enumerate(w.schedule)]
+
+    def step(stream):
+        for c in calls:
+            c.run(stream)
+
+    step(harness.stream_handle())
+    torch.cuda.synchronize()
+    ref_out = [d.out.clone() for d in devs]
+    ref_sup, ref_tags = st.support.clone(), st.tags.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(int(torch.cuda.current_stream().cuda_stream))
+    for it in range(3):
+        for d in devs:
+            d.out.fill_(float("nan"))
+        st.support.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for d, r in zip(devs, ref_out):
+            assert torch.equal(d.out, r), f"replay {it}"
+        assert torch.equal(st.support, ref_sup) and torch.equal(st.tags, ref_tags)
