@@ -27,8 +27,11 @@ Encodings
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
+import threading
 from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
@@ -236,38 +239,103 @@ class LayerInputs:
     num_pages: int
 
 
+class _Scratch(threading.local):
+    """Per-thread reusable buffers (large fresh temporaries in many threads
+    serialize on page faults)."""
+
+    def get(self, name: str, shape, dtype) -> np.ndarray:
+        n = int(np.prod(shape))
+        buf = getattr(self, name, None)
+        if buf is None or buf.size < n or buf.dtype != dtype:
+            buf = np.empty(n, dtype=dtype)
+            setattr(self, name, buf)
+        return buf[:n].reshape(shape)
+
+
+_scratch = _Scratch()
+
+
+def _round_bf16(x: np.ndarray, name: str) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even; the same rounding as
+    f32_to_bf16_bits), overwriting x; return the bit patterns in a contiguous
+    per-thread uint16 buffer."""
+    u = x.view(np.uint32)
+    t = _scratch.get("round_tmp", u.shape, np.uint32)
+    np.right_shift(u, np.uint32(16), out=t)
+    np.bitwise_and(t, np.uint32(1), out=t)
+    np.add(t, np.uint32(0x7FFF), out=t)
+    np.add(u, t, out=u)
+    np.right_shift(u, np.uint32(16), out=t)
+    b = _scratch.get(name, u.shape, np.uint16)
+    np.copyto(b, t, casting="unsafe")
+    return b
+
+
+def _fill_row(w: Workload, depth: int, layer: int, r: int, n: int, bt_row, q, k, v) -> None:
+    """Draw row r (same streams as row_qkv) and write it into q and the pages of k, v."""
+    g = _rng(w.seed, _S_QKV, depth, layer, r)
+    H, d, P = w.heads, w.head_dim, w.page_size
+    qf = g.standard_normal((H, d), dtype=np.float32)
+    K = _scratch.get("K", (H, n, d), np.float32)
+    V = _scratch.get("V", (H, n, d), np.float32)
+    g.standard_normal(out=K, dtype=np.float32)
+    g.standard_normal(out=V, dtype=np.float32)
+    nb = (n + BLOCK - 1) // BLOCK
+    hb = hot_blocks(w, layer, r, nb)
+    for h in range(H):
+        off = np.float32(w.alpha) * (qf[h] / np.float32(np.linalg.norm(qf[h])))
+        for b in hb[h]:
+            K[h, b * BLOCK: min(b * BLOCK + BLOCK, n)] += off
+    q[r] = _encode(qf, w.dtype)
+    for name, src, dst in (("K16", K, k), ("V16", V, v)):
+        e = _round_bf16(src, name) if w.dtype == "bf16" else src
+        for j in range((n + P - 1) // P):
+            lo, hi = j * P, min(n, j * P + P)
+            dst[bt_row[j], :, : hi - lo] = e[:, lo:hi]
+
+
 def layer_inputs(w: Workload, depth: int, layer: int = 0,
-                 rows: Optional[Sequence[int]] = None) -> LayerInputs:
+                 rows: Optional[Sequence[int]] = None, workers: Optional[int] = None) -> LayerInputs:
     """Build the encoded paged inputs of one (depth, layer).
 
-    ``rows`` limits the *filled* rows (others keep poison pages and zero q);
-    shapes and the block table are those of the full workload either way.
+    ``rows`` limits the *filled* rows (others have zero q and pages whose
+    content is undefined); shapes and the block table are those of the full
+    workload either way.  Slots past a filled row's context and spare pages
+    hold the poison pattern.
+    Rows are drawn in parallel threads; every row has its own random stream,
+    so the result does not depend on ``workers``.
     """
     ctx = context_lengths(w)
     bt, num_pages = block_table(w, ctx)
     H, d, P = w.heads, w.head_dim, w.page_size
     enc = np.uint16 if w.dtype == "bf16" else np.float32
     poison = BF16_QNAN if w.dtype == "bf16" else np.float32(np.nan)
-    k = np.full((num_pages, H, P, d), poison, dtype=enc)
-    v = np.full((num_pages, H, P, d), poison, dtype=enc)
+    # Pages of unfilled rows are never read; only the slots no filled row
+    # writes (tails of last pages, spare pages) need the poison pattern.
+    k = np.empty((num_pages, H, P, d), dtype=enc)
+    v = np.empty((num_pages, H, P, d), dtype=enc)
+    used = bt[bt >= 0]
+    spare = np.setdiff1d(np.arange(num_pages), used)
+    k[spare] = poison
+    v[spare] = poison
     q = np.zeros((w.rows, H, d), dtype=enc)
-    todo = range(w.rows) if rows is None else rows
-    for r in todo:
+    todo = list(range(w.rows)) if rows is None else list(rows)
+
+    def fill(r: int) -> None:
         n = int(ctx[r])
-        qf, Kf, Vf = row_qkv(w, depth, layer, r, n)
-        q[r] = _encode(qf, w.dtype)
-        npg = (n + P - 1) // P
-        pad = npg * P - n
-        Ke = _encode(Kf, w.dtype)
-        Ve = _encode(Vf, w.dtype)
-        if pad:
-            Ke = np.concatenate([Ke, np.full((H, pad, d), poison, dtype=enc)], axis=1)
-            Ve = np.concatenate([Ve, np.full((H, pad, d), poison, dtype=enc)], axis=1)
-        Ke = Ke.reshape(H, npg, P, d).transpose(1, 0, 2, 3)
-        Ve = Ve.reshape(H, npg, P, d).transpose(1, 0, 2, 3)
-        pages = bt[r, :npg]
-        k[pages] = Ke
-        v[pages] = Ve
+        _fill_row(w, depth, layer, r, n, bt[r], q, k, v)
+        if n % P:
+            last = bt[r, n // P]
+            k[last, :, n % P:] = poison
+            v[last, :, n % P:] = poison
+
+    nw = workers if workers is not None else min(16, os.cpu_count() or 1, max(1, len(todo)))
+    if nw <= 1:
+        for r in todo:
+            fill(r)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(nw) as ex:
+            list(ex.map(fill, todo))
     return LayerInputs(w, depth, layer, q, k, v, bt, ctx, num_pages)
 
 
