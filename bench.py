@@ -1,11 +1,15 @@
 """Decode-attention throughput of the WISE path on one MI355X.
 
-A step is one token of every row through the workload's depth schedule
-(e.g. discover, discover-union, sparse, sparse) for every layer: each
-(depth, layer) call is the split-KV decode kernel plus the finish kernel.
-The timed region starts with every input resident in HBM.
+A step is one token of every row through the workload's whole hot path:
+for the depth-schedule workloads, every depth (discover, discover-union,
+sparse, sparse) of every layer; for the mixed workload, the one launch that
+mixes dense, discover and sparse rows (after untimed setup depths).  Each
+(depth, layer) call is the split-KV decode kernel (plus the plan kernel
+for calls with sparse rows whose units span several split workgroups) and
+the finish kernel.  Every input is resident in HBM before timing starts.
 
-Prints ONE JSON line (see the design doc for every field).
+Prints ONE JSON line.  ``value`` = decode-attention rows per second, where a
+row is one query row attended at one (depth, layer).
 """
 
 from __future__ import annotations
@@ -27,19 +31,22 @@ from block_sparse_paged_split_amd import harness, synth  # noqa: E402
 from block_sparse_paged_split_amd import wise as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MODE_NAME = {W.WISE_DENSE: "dense", W.WISE_DISCOVER: "discover",
+             W.WISE_DISCOVER_UNION: "discover_union", W.WISE_SPARSE: "sparse"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def split_bytes(w, ctx, mode, support_words, bt_width):
-    """Algorithmic bytes one split-KV launch moves for one (depth, layer).
+def split_bytes(w, ctx, eff_modes, support_words):
+    """Algorithmic bytes one split-KV launch moves.
 
-    Per (row, head): K and V of every attended token (2 * d * e each), q
-    (d * e), and per row the block-table entries of the attended pages.
+    Per (row, head): K and V of every attended token (2 * d * e each) and q
+    (d * e); per row the block-table entries of the pages it reads.
     Discovery rows also write 8 bytes of tile stats per block; sparse rows
-    read their support words.
+    read their support words.  eff_modes[r] is the row's effective mode;
+    support_words [rows, heads, words] is the support a sparse row reads.
     """
     e = 2 if w.dtype == "bf16" else 4
     d, H, P = w.head_dim, w.heads, w.page_size
@@ -47,19 +54,20 @@ def split_bytes(w, ctx, mode, support_words, bt_width):
     for r in range(w.rows):
         n = int(ctx[r])
         nb = (n + 31) // 32
-        pages = (n + P - 1) // P
-        total += pages * 4
-        for h in range(H):
-            if mode == W.WISE_SPARSE:
-                bits = support_words[r, h]
-                blocks = [b for b in range(nb) if (int(bits[b >> 5]) >> (b & 31)) & 1]
-                toks = sum(min(32, n - 32 * b) for b in blocks)
-                total += 4 * ((nb + 31) // 32)
-            else:
-                toks = n
-                if mode != W.WISE_DENSE:
-                    total += 8 * nb
-            total += 2 * toks * d * e + d * e
+        mode = int(eff_modes[r])
+        if mode == W.WISE_SPARSE:
+            b = np.arange(nb)
+            bits = ((support_words[r][:, b >> 5] >> (b & 31).astype(np.uint32)) & 1).astype(bool)
+            tok_per_block = np.minimum(32, n - 32 * b)
+            toks = (bits * tok_per_block[None, :]).sum(axis=1)          # [H]
+            pages = set()
+            for blk in np.nonzero(bits.any(axis=0))[0]:
+                pages.update(range((32 * blk) // P, (min(n, 32 * blk + 32) - 1) // P + 1))
+            total += int(2 * toks.sum() * d * e) + H * d * e + H * 4 * ((nb + 31) // 32) + 4 * len(pages)
+        else:
+            total += H * (2 * n * d * e + d * e) + 4 * ((n + P - 1) // P)
+            if mode != W.WISE_DENSE:
+                total += H * 8 * nb
     return total
 
 
@@ -96,19 +104,90 @@ def cpu_baseline(w, min_s=10.0, max_rows=32):
                       f"repeats = {rows_done} row-calls in {t_total:.1f} s (fp64 numpy, 1 BLAS thread)"}
 
 
+class Plan:
+    """The calls of one step, per replica, and how to account for them."""
+
+    def __init__(self, w, args, dev):
+        import torch
+        self.w = w
+        self.ctx = synth.context_lengths(w)
+        self.mixed = w.name == "ctx8k_mixed"
+        # distinct KV sets: replicas x depths x (layer groups)
+        self.kv_layers = min(w.layers, args.kv_layers)
+        self.replicas = args.replicas
+        self.state = harness.SupportState(w.rows, w.heads, w.max_ctx, layers=w.layers, device=dev)
+        self.ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx, device=dev)
+        self.kv = {}
+        t0 = time.time()
+        depths = 3 if self.mixed else len(w.schedule)
+        for rep in range(self.replicas):
+            for depth in range(depths):
+                for lg in range(self.kv_layers):
+                    wl = dataclasses.replace(w, seed=w.seed + 1000 * rep)
+                    self.kv[(rep, depth, lg)] = harness.upload(synth.layer_inputs(wl, depth, lg), device=dev)
+                    log(f"inputs: replica {rep} depth {depth} layer-set {lg} ({time.time() - t0:.1f} s)")
+        if self.mixed:
+            modes, flagged = synth.mixed_row_modes(w)
+            self.row_modes = modes
+            self.flagged = flagged
+            d0 = np.where(modes == W.WISE_DENSE, W.WISE_DENSE, W.WISE_DISCOVER).astype(np.uint8)
+            d1 = np.where((modes == W.WISE_SPARSE) & ~flagged, W.WISE_DISCOVER_UNION,
+                          W.WISE_DENSE).astype(np.uint8)
+            self.setup_modes = [torch.from_numpy(d0).to(dev), torch.from_numpy(d1).to(dev)]
+            self.mixed_modes = torch.from_numpy(modes.astype(np.uint8)).to(dev)
+        # calls[rep] = list of (PreparedCall, key) for one step
+        self.calls = {}
+        for rep in range(self.replicas):
+            lst = []
+            if self.mixed:
+                pc = harness.PreparedCall(self.kv[(rep, 2, 0)], self.ws, W.WISE_SPARSE, self.state,
+                                          required=w.discoveries, eta=w.eta, row_mode=self.mixed_modes)
+                lst.append((pc, ("mixed", 2, 0)))
+            else:
+                for depth, mode in enumerate(w.schedule):
+                    for layer in range(w.layers):
+                        pc = harness.PreparedCall(self.kv[(rep, depth, layer % self.kv_layers)], self.ws, mode,
+                                                  self.state, layer_idx=layer, required=w.discoveries, eta=w.eta)
+                        lst.append((pc, (MODE_NAME[mode], depth, layer)))
+            self.calls[rep] = lst
+        self.calls_per_step = len(self.calls[0])
+
+    def setup(self, rep, stream):
+        """Untimed depths that precede the mixed launch (discovery of its rows)."""
+        if not self.mixed:
+            return
+        for depth in (0, 1):
+            harness.PreparedCall(self.kv[(rep, depth, 0)], self.ws, W.WISE_SPARSE, self.state,
+                                 required=self.w.discoveries, eta=self.w.eta,
+                                 row_mode=self.setup_modes[depth]).run(stream)
+
+    def eff_modes(self, key):
+        w = self.w
+        if key[0] == "mixed":
+            eff = self.row_modes.copy()
+            eff[self.flagged] = W.WISE_DENSE
+            return eff
+        mode = {v: k for k, v in MODE_NAME.items()}[key[0]]
+        return np.full(w.rows, mode)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ctx1k", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--replicas", type=int, default=2,
-                    help="distinct KV sets per depth, rotated so the 256 MB MALL cannot serve repeats")
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="distinct KV sets per depth, rotated across steps so the 256 MB MALL cannot "
+                         "serve repeats (default: 2 when one set is under 1 GB, else 1)")
+    ap.add_argument("--kv-layers", type=int, default=3,
+                    help="distinct KV sets per depth for multi-layer workloads, rotated over the layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-reference", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -116,42 +195,30 @@ def main():
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    # ---- inputs: every (replica, depth) KV set resident in HBM ----
-    t0 = time.time()
-    layers = {}
-    for rep in range(args.replicas):
-        for depth in range(len(w.schedule)):
-            li = synth.layer_inputs(dataclasses.replace(w, seed=w.seed + 1000 * rep), depth)
-            layers[(rep, depth)] = harness.upload(li, device=dev)
-            log(f"inputs: replica {rep} depth {depth} uploaded ({time.time() - t0:.1f} s)")
-    ctx = synth.context_lengths(w)
-    bt_width = layers[(0, 0)].block_table.shape[1]
-    state = harness.SupportState(w.rows, w.heads, w.max_ctx, device=dev)
-    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx, device=dev)
-    calls = len(w.schedule) * w.layers
-    prepared = {(rep, depth): harness.PreparedCall(layers[(rep, depth)], ws, mode, state,
-                                                   required=w.discoveries, eta=w.eta)
-                for rep in range(args.replicas) for depth, mode in enumerate(w.schedule)}
+    if args.replicas is None:
+        one_set = int(synth.context_lengths(w).sum()) * w.heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
+        args.replicas = 2 if one_set < (1 << 30) else 1
+    plan = Plan(w, args, dev)
+    calls = plan.calls_per_step
     ev = harness.HipEvents(2 * calls * args.steps)
-
-    def step(i, stream, timed=False):
-        rep = i % args.replicas
-        for depth in range(len(w.schedule)):
-            pc = prepared[(rep, depth)]
-            for layer in range(w.layers):
-                c = 2 * (i * calls + depth * w.layers + layer)
-                pc.set_events(ev.handle(c), ev.handle(c + 1)) if timed else pc.set_events(None, None)
-                pc.run(stream)
-
     main_stream = torch.cuda.current_stream()
     sh = int(main_stream.cuda_stream)
+
+    def step(i, stream, timed=False):
+        rep = i % plan.replicas
+        for c, (pc, _) in enumerate(plan.calls[rep]):
+            k = 2 * (i * calls + c)
+            pc.set_events(ev.handle(k), ev.handle(k + 1)) if timed else pc.set_events(None, None)
+            pc.run(stream)
+
+    for rep in range(plan.replicas):
+        plan.setup(rep, sh)
     for i in range(args.warmup):
         step(i, sh)
     torch.cuda.synchronize()
 
     # ---- timed region 1 (eager): every split-KV launch bracketed by HIP events ----
-    state.counters.zero_()
+    plan.state.counters.zero_()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -161,51 +228,52 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     eager_ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    ctr = state.counters.cpu().numpy().copy()
+    ctr = plan.state.counters.cpu().numpy().copy()
 
     # ---- timed region 2: the same steps replayed from HIP graphs ----
     graphs = []
-    for rep in range(args.replicas):
+    for rep in range(plan.replicas):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(rep, int(torch.cuda.current_stream().cuda_stream))
         graphs.append(g)
     for i in range(args.warmup):
-        graphs[i % args.replicas].replay()
+        graphs[i % plan.replicas].replay()
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
-        graphs[i % args.replicas].replay()
+        graphs[i % plan.replicas].replay()
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
     # ---- per-mode split-kernel times and algorithmic bytes ----
-    # the support a sparse depth reads is the one its replica's discovery
+    # the support a sparse call reads is the one its replica's discovery
     # depths wrote in the same step: rebuild it per replica (untimed)
     sup_of = {}
-    for rep in range(args.replicas):
+    for rep in range(plan.replicas):
+        plan.setup(rep, sh)
         step(rep, sh)
         torch.cuda.synchronize()
-        sup_of[rep] = state.support_numpy()[:, 0].copy()
+        sup_of[rep] = plan.state.support_numpy().copy()
     per_mode = {}
-    for depth, mode in enumerate(w.schedule):
-        key = {W.WISE_DENSE: "dense", W.WISE_DISCOVER: "discover",
-               W.WISE_DISCOVER_UNION: "discover_union", W.WISE_SPARSE: "sparse"}[mode]
-        m = per_mode.setdefault(key, {"ms": [], "bytes": []})
-        nb_of = {rep: split_bytes(w, ctx, mode, sup_of[rep], bt_width) for rep in range(args.replicas)}
-        for i in range(args.steps):
-            for layer in range(w.layers):
-                c = 2 * (i * calls + depth * w.layers + layer)
-                m["ms"].append(ev.elapsed_ms(c, c + 1))
-                m["bytes"].append(nb_of[i % args.replicas])
+    bytes_cache = {}
+    for i in range(args.steps):
+        rep = i % plan.replicas
+        for c, (pc, key) in enumerate(plan.calls[rep]):
+            name, depth, layer = key
+            ck = (rep, name, layer)
+            if ck not in bytes_cache:
+                bytes_cache[ck] = split_bytes(w, plan.ctx, plan.eff_modes(key), sup_of[rep][:, layer])
+            m = per_mode.setdefault(name, {"ms": [], "bytes": []})
+            m["ms"].append(ev.elapsed_ms(2 * (i * calls + c), 2 * (i * calls + c) + 1))
+            m["bytes"].append(bytes_cache[ck])
     modes_out = {}
     tot_bytes = tot_ms = 0.0
     for key, m in per_mode.items():
         ms = np.asarray(m["ms"])
         by = np.asarray(m["bytes"], dtype=np.float64)
-        avg = float(ms.mean())
-        modes_out[key] = {"split_us": round(avg * 1e3, 2),
+        modes_out[key] = {"split_us": round(float(ms.mean()) * 1e3, 2),
                           "split_us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
                           "split_us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2),
                           "algorithmic_MB": round(float(by.mean()) / 1e6, 3),
@@ -213,6 +281,29 @@ def main():
         tot_bytes += float(by.sum())
         tot_ms += float(ms.sum())
     achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
+
+    # ---- dense reference on the KV each sparse or mixed call reads (same data) ----
+    if not args.no_dense_reference:
+        refs = [(pc, key) for pc, key in plan.calls[0] if key[0] in ("sparse", "mixed")][:4]
+        ev2 = harness.HipEvents(2)
+        dense_ms = []
+        for pc, key in refs:
+            layer_dev = plan.kv[(0, key[1], key[2] % plan.kv_layers)]
+            dpc = harness.PreparedCall(layer_dev, plan.ws, W.WISE_DENSE)
+            for it in range(12):
+                dpc.set_events(ev2.handle(0), ev2.handle(1)) if it >= 2 else dpc.set_events(None, None)
+                dpc.run(sh)
+                if it >= 2:
+                    torch.cuda.synchronize()
+                    dense_ms.append(ev2.elapsed_ms(0, 1))
+        if dense_ms:
+            dms = float(np.median(dense_ms))
+            dbytes = split_bytes(w, plan.ctx, np.full(w.rows, W.WISE_DENSE), None)
+            key = "mixed" if plan.mixed else "sparse"
+            modes_out["dense_same_kv"] = {"split_us": round(dms * 1e3, 2), "algorithmic_MB": round(dbytes / 1e6, 3),
+                                          "GBps": round(dbytes / (dms * 1e-3) / 1e9, 1)}
+            modes_out[key]["speedup_vs_dense"] = round(dms * 1e3 / modes_out[key]["split_us"], 3)
+
     rows_per_step = w.rows * calls
     out = {
         "metric": "decode-attn rows/s + achieved HBM GB/s (sparse vs dense), ctx 1K/4K/8K",
@@ -224,12 +315,15 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "rows": w.rows, "heads": w.heads, "head_dim": w.head_dim,
-                   "ctx": w.ctx if w.ctx else "ragged", "page_size": w.page_size,
-                   "layers": w.layers, "schedule": list(w.schedule), "eta": w.eta,
-                   "row_calls_per_step": rows_per_step, "kv_replicas": args.replicas,
+                   "ctx": w.ctx if w.ctx else f"{int(plan.ctx.min())}..{int(plan.ctx.max())}",
+                   "page_size": w.page_size, "layers": w.layers,
+                   "schedule": "mixed launch" if plan.mixed else list(w.schedule), "eta": w.eta,
+                   "row_calls_per_step": rows_per_step, "kv_replicas": plan.replicas,
+                   "kv_sets_per_depth": plan.kv_layers,
                    "timing": "HIP graph replay of whole steps",
                    "union_density": round(float(ctr[W.CTR_SELECTED] / max(1, ctr[W.CTR_CAUSAL])), 4),
-                   "fallbacks": int(ctr[W.CTR_FALLBACKS]), "errors": int(ctr[W.CTR_ERRORS])},
+                   "fallbacks_per_step": round(float(ctr[W.CTR_FALLBACKS]) / args.steps, 2),
+                   "errors": int(ctr[W.CTR_ERRORS])},
         "modes": modes_out,
         "roofline": {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -354,11 +354,24 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
   __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u = blockIdx.x / p.chunk_groups;                                // unit = (row, head)
-  const int k = (blockIdx.x - u * p.chunk_groups) * kWavesPerGroup + wave;  // item slot
+  // Workgroup i runs on XCD i % 8.  Group-major order (i = group * units +
+  // unit) keeps every unit on XCD unit % 8 for all its groups, so each row's
+  // heads spread over all XCDs however short the row is (unit-major order
+  // would pile the only non-empty group of short rows onto one XCD).
+  const int units = p.rows * p.heads;
+  const int grp = blockIdx.x / units;
+  const int u = blockIdx.x - grp * units;           // unit = (row, head)
+  const int k = grp * kWavesPerGroup + wave;        // item slot
   if (k >= p.items_per_unit) return;
   const int r = u / p.heads;
   const int h = u - r * p.heads;
+  if (k > 0) {
+    // No mode gives a row more tiles than its causal blocks: slots past them
+    // leave after one load (rows far shorter than max_ctx leave most slots empty).
+    const int n0 = p.ctx_len[r];
+    const int nb0 = (n0 >= 1 && n0 <= p.max_ctx) ? (n0 + kBlock - 1) / kBlock : 0;
+    if (k >= (nb0 + p.tiles_per_item - 1) / p.tiles_per_item) return;
+  }
   const RowPlan rp = plan_row(p, r);
   const int nb = rp.bad ? 0 : (rp.n + kBlock - 1) / kBlock;
   const bool sparse = !rp.bad && rp.eff == WISE_SPARSE;
