@@ -104,6 +104,30 @@ def cpu_baseline(w, min_s=10.0, max_rows=32):
                       f"repeats = {rows_done} row-calls in {t_total:.1f} s (fp64 numpy, 1 BLAS thread)"}
 
 
+def split_source_digest() -> str:
+    import hashlib
+    src = os.path.join(ROOT, "block_sparse_paged_split_amd", "csrc", "wise_split.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per split launch from the committed counter summary of this
+    workload, or None when there is none or the split kernel's source has
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)
+    except (IndexError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != split_source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 class Plan:
     """The calls of one step, per replica, and how to account for them."""
 
@@ -184,6 +208,11 @@ def main():
                     help="distinct KV sets per depth for multi-layer workloads, rotated over the layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-reference", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (for counter-collection runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run one plain device-to-device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -198,6 +227,14 @@ def main():
     if args.replicas is None:
         one_set = int(synth.context_lengths(w).sum()) * w.heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
         args.replicas = 2 if one_set < (1 << 30) else 1
+    if args.calibrate_copy:
+        # a plain streaming kernel of known size (reads and writes MIB MiB)
+        src = torch.zeros(args.calibrate_copy << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration kernel (neg): {args.calibrate_copy} MiB read + {args.calibrate_copy} MiB written")
+        del src, dst
     plan = Plan(w, args, dev)
     calls = plan.calls_per_step
     ev = harness.HipEvents(2 * calls * args.steps)
@@ -231,21 +268,24 @@ def main():
     ctr = plan.state.counters.cpu().numpy().copy()
 
     # ---- timed region 2: the same steps replayed from HIP graphs ----
-    graphs = []
-    for rep in range(plan.replicas):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(rep, int(torch.cuda.current_stream().cuda_stream))
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % plan.replicas].replay()
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        graphs[i % plan.replicas].replay()
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    if args.no_graph:
+        ms_per_step = eager_ms_per_step
+    else:
+        graphs = []
+        for rep in range(plan.replicas):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(rep, int(torch.cuda.current_stream().cuda_stream))
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % plan.replicas].replay()
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(args.steps):
+            graphs[i % plan.replicas].replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
     # ---- per-mode split-kernel times and algorithmic bytes ----
     # the support a sparse call reads is the one its replica's discovery
@@ -320,14 +360,14 @@ def main():
                    "schedule": "mixed launch" if plan.mixed else list(w.schedule), "eta": w.eta,
                    "row_calls_per_step": rows_per_step, "kv_replicas": plan.replicas,
                    "kv_sets_per_depth": plan.kv_layers,
-                   "timing": "HIP graph replay of whole steps",
+                   "timing": "eager launches" if args.no_graph else "HIP graph replay of whole steps",
                    "union_density": round(float(ctr[W.CTR_SELECTED] / max(1, ctr[W.CTR_CAUSAL])), 4),
                    "fallbacks_per_step": round(float(ctr[W.CTR_FALLBACKS]) / args.steps, 2),
                    "errors": int(ctr[W.CTR_ERRORS])},
         "modes": modes_out,
         "roofline": {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

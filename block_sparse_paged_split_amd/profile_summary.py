@@ -1,0 +1,119 @@
+"""Summaries of rocprofv3 output for profiles/ (text only).
+
+kernel-stats: rocprofv3 --kernel-trace --stats --output-format csv run
+    -> a markdown table of per-kernel calls and durations.
+traffic: two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of a bench
+    command with --calibrate-copy MIB -> HBM bytes per split launch, each
+    counter scaled by what it reads for the calibration kernel (neg over
+    MIB MiB of fp32: MIB MiB read, MIB MiB written).
+
+Usage:
+  python -m block_sparse_paged_split_amd.profile_summary kernel-stats STATS_CSV OUT_MD --command CMD
+  python -m block_sparse_paged_split_amd.profile_summary traffic FETCH_CSV WRITE_CSV OUT_MD \
+      --workload W --calibrate-mib MIB --algorithmic-bytes B --command CMD --command CMD
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def split_source_digest() -> str:
+    return hashlib.sha256(open(os.path.join(PKG, "csrc", "wise_split.hip"), "rb").read()).hexdigest()
+
+
+def short(name: str) -> str:
+    for key in ("split_static_kernel", "split_listed_kernel", "plan_kernel", "finish_kernel"):
+        if key in name:
+            tmpl = name[name.find("<"): name.find(">") + 1] if "<" in name else ""
+            return key + tmpl
+    return name if len(name) < 70 else name[:67] + "..."
+
+
+def kernel_stats(stats_csv: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel durations: rocprofv3 --kernel-trace --stats", "",
+             "Command (run from /tmp with TMPDIR=/tmp; R = the repository root):", "",
+             "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def _per_kernel(counter_csv: str, counter: str):
+    vals = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if r.get("Counter_Name") != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(fetch_csv: str, write_csv: str, out_md: str, workload: str, mib: int, algo: float,
+            commands) -> None:
+    f = _per_kernel(fetch_csv, "FETCH_SIZE")
+    w = _per_kernel(write_csv, "WRITE_SIZE")
+    known = mib * 1024.0  # KiB read by the calibration kernel, and KiB written
+    cal_f = [v for k, v in f.items() if "neg" in k.lower()]
+    cal_w = [v for k, v in w.items() if "neg" in k.lower()]
+    if not cal_f or not cal_w:
+        raise SystemExit("calibration kernel not found in the counter output")
+    scale_f = known / max(cal_f[0])
+    scale_w = known / max(cal_w[0])
+    split = [k for k in f if "split_" in k and "kernel" in k]
+    fk = [x for k in split for x in f[k]]
+    wk = [x for k in split for x in w.get(k, [])]
+    fetch_kib = sum(fk) / len(fk)
+    write_kib = sum(wk) / len(wk) if wk else 0.0
+    traffic_bytes = (fetch_kib * scale_f + write_kib * scale_w) * 1024.0
+    rec = {"workload": workload, "kernel_source_sha256": split_source_digest(),
+           "split_launches": len(fk), "fetch_kib_per_launch": round(fetch_kib, 1),
+           "write_kib_per_launch": round(write_kib, 1),
+           "calibration_mib": mib, "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4),
+           "traffic_bytes_per_launch": round(traffic_bytes),
+           "algorithmic_bytes_per_launch": round(algo),
+           "traffic_over_algorithmic": round(traffic_bytes / algo, 4) if algo else None}
+    lines = [f"# HBM traffic of the split-KV kernel: {workload}", "",
+             "Two counter runs of the same bench command (FETCH_SIZE, then WRITE_SIZE, KiB per",
+             "dispatch summed over the L2 channels), each scaled by what the counter reads for the",
+             f"calibration kernel (neg over {mib} MiB of fp32: {mib} MiB read, {mib} MiB written).",
+             "bench.py reports traffic_bytes_per_launch as roofline.traffic while the split",
+             "kernel source still hashes to kernel_source_sha256.", "", "Commands:", "", "```"]
+    lines += list(commands) + ["```", "", "```json", json.dumps(rec, indent=1), "```", ""]
+    open(out_md, "w").write("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("kernel-stats")
+    a.add_argument("stats_csv")
+    a.add_argument("out_md")
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("out_md")
+    b.add_argument("--workload", required=True)
+    b.add_argument("--calibrate-mib", type=int, required=True)
+    b.add_argument("--algorithmic-bytes", type=float, required=True)
+    b.add_argument("--command", action="append", default=[])
+    args = ap.parse_args()
+    if args.what == "kernel-stats":
+        kernel_stats(args.stats_csv, args.out_md, args.command)
+    else:
+        traffic(args.fetch_csv, args.write_csv, args.out_md, args.workload, args.calibrate_mib,
+                args.algorithmic_bytes, args.command)
+
+
+if __name__ == "__main__":
+    main()
