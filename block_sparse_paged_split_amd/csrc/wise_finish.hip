@@ -65,10 +65,12 @@ __device__ __forceinline__ float key_mass(unsigned long long key) {
   return __uint_as_float(static_cast<uint32_t>(key >> 32));
 }
 
-// Selection of one discovery unit with KPL keys per lane (64*KPL >= nb).
-// Returns K; sets the selected blocks' bits in s_bits.
+// Block masses of one discovery unit from its tile stats (loaded by the
+// caller, lane l holding blocks l*KPL .. l*KPL+KPL-1), sorted descending by
+// (mass, ~block index) with a bitonic network held in registers; the fp64
+// running sum picks K; the selected blocks' bits are ORed into s_bits.
 template <int KPL>
-__device__ __forceinline__ int select_eta(const float2 *st, float eta, int nb, float M, float L, int lane,
+__device__ __forceinline__ int select_eta(const float2 (&st)[KPL], float eta, int nb, float M, float L, int lane,
                                           uint32_t *s_bits) {
   unsigned long long key[KPL];
   const float invL = 1.0f / L;
@@ -77,8 +79,7 @@ __device__ __forceinline__ int select_eta(const float2 *st, float eta, int nb, f
     const int b = lane * KPL + j;
     key[j] = 0ull;  // padding sorts after every block
     if (b < nb) {
-      const float2 ml = st[b];
-      const float mass = ml.y * __builtin_amdgcn_exp2f(ml.x - M) * invL;
+      const float mass = st[j].y * __builtin_amdgcn_exp2f(st[j].x - M) * invL;
       key[j] = (static_cast<unsigned long long>(__float_as_uint(mass)) << 32) |
                static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(b));
     }
@@ -143,25 +144,26 @@ __device__ __forceinline__ int select_eta(const float2 *st, float eta, int nb, f
   return K;
 }
 
-__global__ __launch_bounds__(kLanes) void finish_kernel(const FinishParams p) {
-  __shared__ float s_w[kMaxItemsPerUnit];
-  __shared__ uint32_t s_bits[kMaxWords];
+// Row facts the finish of one unit needs (all from scalar loads issued together).
+struct UnitInfo {
+  int u, r, h, eff, req, items, nb, slot;
+  bool row_bad;
+};
 
+// Finish of one unit.  Every load that does not depend on arithmetic (item
+// partials, tile stats, old support words) is issued up front, so the
+// discovery path waits on memory about once instead of once per step.
+template <int KPL>
+__device__ __forceinline__ void finish_unit(const FinishParams &p, const UnitInfo &ui, float *s_w,
+                                            uint32_t *s_bits) {
   const int lane = threadIdx.x;
-  const int u = blockIdx.x;
-  const int r = u / p.heads;
-  const int h = u - r * p.heads;
-  const int code = p.row_code[r];
-  const int eff = code & 0xF;
-  const int req = (code >> 4) & 0xF;
-  const bool row_bad = eff == kRowError;
-  const int items = row_bad ? 0 : p.unit_items[u];
-  const int64_t base = static_cast<int64_t>(u) * p.items_per_unit;
+  const int items = ui.items;
+  const int64_t base = static_cast<int64_t>(ui.u) * p.items_per_unit;
   const int D = p.head_dim;
+  const bool stateful = p.support != nullptr && !ui.row_bad && ui.req != WISE_DENSE;
+  const bool discover = stateful && (ui.eff == WISE_DISCOVER || ui.eff == WISE_DISCOVER_UNION);
 
-  // ---- 1. merge ----
-  // The accumulators of the first kUnroll items do not depend on the merge
-  // weights: their loads go out first, together with the (m, l) loads.
+  // ---- loads: partials, tile stats, old support words ----
   constexpr int kDims = 2;  // head_dim <= 2 * 64
   const float *acc = p.part_acc + base * D;
   float v[kDims][kUnroll];
@@ -172,12 +174,28 @@ __global__ __launch_bounds__(kLanes) void finish_kernel(const FinishParams p) {
     for (int t = 0; t < kUnroll; ++t) v[q][t] = (dd < D && t < items) ? acc[t * D + dd] : 0.0f;
   }
   float2 ml_own[kMaxItemsPerUnit / kLanes];
-  float M = -INFINITY;
-  bool bad_item = false;
 #pragma unroll
   for (int c = 0; c < kMaxItemsPerUnit / kLanes; ++c) {
     const int i = c * kLanes + lane;
     ml_own[c] = i < items ? p.part_ml[base + i] : make_float2(-INFINITY, 0.0f);
+  }
+  float2 st[KPL];
+  const float2 *stp = p.stats + static_cast<int64_t>(ui.u) * p.max_blocks;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int b = lane * KPL + j;
+    st[j] = (discover && b < ui.nb) ? stp[b] : make_float2(0.0f, 0.0f);
+  }
+  uint32_t *sw = discover ? p.support + ((static_cast<int64_t>(ui.slot) * p.layers + p.layer) * p.heads + ui.h) *
+                                             p.words
+                          : nullptr;
+  const uint32_t old_word = (discover && ui.eff == WISE_DISCOVER_UNION && lane < p.words) ? sw[lane] : 0u;
+
+  // ---- 1. merge: M, w_i, L, out (fixed orders) ----
+  float M = -INFINITY;
+  bool bad_item = false;
+#pragma unroll
+  for (int c = 0; c < kMaxItemsPerUnit / kLanes; ++c) {
     bad_item |= ml_own[c].y < 0.0f;
     M = fmaxf(M, ml_own[c].x);
   }
@@ -194,6 +212,8 @@ __global__ __launch_bounds__(kLanes) void finish_kernel(const FinishParams p) {
     }
   }
   const float L = wave_sum(Lp);
+  if (discover)
+    for (int w = lane; w < kMaxWords; w += kLanes) s_bits[w] = 0u;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kDims; ++q) {
@@ -211,73 +231,85 @@ __global__ __launch_bounds__(kLanes) void finish_kernel(const FinishParams p) {
       for (int t = 0; t < kUnroll; ++t)
         if (i0 + t < items) a = fmaf(x[t], s_w[i0 + t], a);
     }
-    p.out[static_cast<int64_t>(u) * D + dd] = err ? __builtin_nanf("") : a / L;
+    p.out[static_cast<int64_t>(ui.u) * D + dd] = err ? __builtin_nanf("") : a / L;
   }
   if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
 
-  if (p.support == nullptr || row_bad || req == WISE_DENSE) return;
-  const int slot = p.slot_of_row ? p.slot_of_row[r] : r;
-  const bool discover = eff == WISE_DISCOVER || eff == WISE_DISCOVER_UNION;
+  if (!stateful) return;
+  const int slot = ui.slot;
   wise_tag *tag = p.tags + static_cast<int64_t>(slot) * p.layers + p.layer;
-
   if (!discover) {
     // a union row whose discovery window is broken ran dense: the rest of
     // this token runs dense too
-    if (req == WISE_DISCOVER_UNION && h == 0 && lane == 0) tag->discoveries = 0;
+    if (ui.req == WISE_DISCOVER_UNION && ui.h == 0 && lane == 0) tag->discoveries = 0;
     return;
   }
 
   // ---- 2. eta selection, 3. support write / union ----
-  const int nb = (p.ctx_len[r] + kBlock - 1) / kBlock;
   int selected = 0;
   if (!err) {
-    for (int w = lane; w < kMaxWords; w += kLanes) s_bits[w] = 0u;
+    const int K = select_eta<KPL>(st, p.eta, ui.nb, M, L, lane, s_bits);
     __syncthreads();
-    const float2 *st = p.stats + static_cast<int64_t>(u) * p.max_blocks;
-    const float eta = p.eta;
-    int K;
-    if (nb <= kLanes) K = select_eta<1>(st, eta, nb, M, L, lane, s_bits);
-    else if (nb <= 2 * kLanes) K = select_eta<2>(st, eta, nb, M, L, lane, s_bits);
-    else if (nb <= 4 * kLanes) K = select_eta<4>(st, eta, nb, M, L, lane, s_bits);
-    else if (nb <= 8 * kLanes) K = select_eta<8>(st, eta, nb, M, L, lane, s_bits);
-    else if (nb <= 16 * kLanes) K = select_eta<16>(st, eta, nb, M, L, lane, s_bits);
-    else K = select_eta<32>(st, eta, nb, M, L, lane, s_bits);
-    __syncthreads();
-    uint32_t *sw = p.support + ((static_cast<int64_t>(slot) * p.layers + p.layer) * p.heads + h) * p.words;
     int added = 0;
     for (int w = lane; w < p.words; w += kLanes) {
       const uint32_t nw = w < kMaxWords ? s_bits[w] : 0u;
-      if (eff == WISE_DISCOVER) {
+      if (ui.eff == WISE_DISCOVER) {
         sw[w] = nw;
       } else {
-        const uint32_t old = sw[w];
+        const uint32_t old = w == lane ? old_word : sw[w];
         sw[w] = old | nw;
         added += __popc(nw & ~old);
       }
     }
-    selected = eff == WISE_DISCOVER ? K : wave_sum_int(added);
+    selected = ui.eff == WISE_DISCOVER ? K : wave_sum_int(added);
   }
 
   // ---- the row's tag and density counts: by the last of its heads to arrive ----
   if (lane != 0) return;
   const unsigned long long mine =
       1ull | (err ? (1ull << 16) : 0ull) | (static_cast<unsigned long long>(selected) << 32);
-  const unsigned long long all = atomicAdd(p.row_done + r, mine) + mine;
+  const unsigned long long all = atomicAdd(p.row_done + ui.r, mine) + mine;
   if (static_cast<int>(all & 0xFFFFull) != p.heads) return;
   const int err_heads = static_cast<int>((all >> 16) & 0xFFFFull);
   if (p.counters) {
     atomicAdd(p.counters + WISE_CTR_SELECTED, all >> 32);
-    if (eff == WISE_DISCOVER)
-      atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(nb) * (p.heads - err_heads));
+    if (ui.eff == WISE_DISCOVER)
+      atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(ui.nb) * (p.heads - err_heads));
   }
   // a bad page in any head of the row breaks this discovery
-  if (eff == WISE_DISCOVER) {
-    tag->request = p.row_request[r];
-    tag->position = p.row_position[r];
+  if (ui.eff == WISE_DISCOVER) {
+    tag->request = p.row_request[ui.r];
+    tag->position = p.row_position[ui.r];
     tag->discoveries = err_heads ? 0 : 1;
   } else {
     tag->discoveries = err_heads ? 0 : tag->discoveries + 1;
   }
+}
+
+__global__ __launch_bounds__(kLanes) void finish_kernel(const FinishParams p) {
+  __shared__ float s_w[kMaxItemsPerUnit];
+  __shared__ uint32_t s_bits[kMaxWords];
+  UnitInfo ui;
+  ui.u = blockIdx.x;
+  ui.r = ui.u / p.heads;
+  ui.h = ui.u - ui.r * p.heads;
+  // independent scalar loads, issued together
+  const int code = p.row_code[ui.r];
+  const int items = p.unit_items[ui.u];
+  const int n = p.ctx_len[ui.r];
+  const int slot = (p.support && p.slot_of_row) ? p.slot_of_row[ui.r] : ui.r;
+  ui.eff = code & 0xF;
+  ui.req = (code >> 4) & 0xF;
+  ui.row_bad = ui.eff == kRowError;
+  ui.items = ui.row_bad ? 0 : items;
+  ui.nb = ui.row_bad ? 0 : (n + kBlock - 1) / kBlock;
+  ui.slot = slot;
+  if (ui.nb <= kLanes) finish_unit<1>(p, ui, s_w, s_bits);
+  else if (ui.nb <= 2 * kLanes) finish_unit<2>(p, ui, s_w, s_bits);
+  else if (ui.nb <= 4 * kLanes) finish_unit<4>(p, ui, s_w, s_bits);
+  else if (ui.nb <= 8 * kLanes) finish_unit<8>(p, ui, s_w, s_bits);
+  else if (ui.nb <= 16 * kLanes) finish_unit<16>(p, ui, s_w, s_bits);
+  else finish_unit<32>(p, ui, s_w, s_bits);
 }
 
 }  // namespace

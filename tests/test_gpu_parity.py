@@ -275,3 +275,37 @@ def test_graph_replay_matches_eager(torch):
         for d, r in zip(devs, ref_out):
             assert torch.equal(d.out, r), f"replay {it}"
         assert torch.equal(st.support, ref_sup) and torch.equal(st.tags, ref_tags)
+
+
+def test_graph_replay_mixed_planned_launch(torch):
+    """A mixed launch that takes the planned path (plan kernel + persistent
+    split over the compact item list) replays from a HIP graph bit for bit."""
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=8, ctx=4096, name="graph_mixed4k")
+    say("[graph_mixed4k] capture discover + mixed launch, replay x3")
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    d0 = harness.upload(synth.layer_inputs(w, 0))
+    d1 = harness.upload(synth.layer_inputs(w, 1))
+    modes = torch.tensor([0, 1, 2, 3, 3, 3, 2, 1], dtype=torch.uint8, device="cuda")
+    calls = [harness.PreparedCall(d0, ws, W.WISE_DISCOVER, st, required=1),
+             harness.PreparedCall(d1, ws, W.WISE_SPARSE, st, required=1, row_mode=modes)]
+
+    def step(stream):
+        for c in calls:
+            c.run(stream)
+
+    step(harness.stream_handle())
+    torch.cuda.synchronize()
+    ref = (d0.out.clone(), d1.out.clone(), st.support.clone(), st.tags.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(int(torch.cuda.current_stream().cuda_stream))
+    for it in range(3):
+        d0.out.fill_(float("nan"))
+        d1.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (d0.out, d1.out, st.support, st.tags)
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {it}"
