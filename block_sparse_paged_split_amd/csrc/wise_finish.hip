@@ -9,7 +9,8 @@
 // first discovery depth, its selection and the causal blocks, and for a
 // union depth only the newly set blocks.
 //
-// One wave64 per (row, head):
+// One workgroup per row (a row with more than 16 heads takes several), one
+// wave64 per (row, head):
 //  1. merge the unit's items: M = max m_i, w_i = 2^(m_i - M),
 //     L = sum l_i w_i, out = sum acc_i w_i / L (fixed summation orders; the
 //     loads of up to eight items are in flight together);
@@ -19,11 +20,14 @@
 //     [l*KPL, l*KPL+KPL)); running sum in fp64 (per-lane run, then a wave
 //     scan); K = the first prefix reaching eta, at least 1, all blocks if
 //     rounding never reaches eta;
-//  3. write (DISCOVER) or OR (DISCOVER_UNION) the unit's support words; each
-//     head adds (1 arrival, error flag, selected blocks) to its row's atomic
-//     word, and the last head to arrive updates the row's tag and adds the
-//     row's totals to the density counters (one global atomic per row, not
-//     per head).
+//  3. write (DISCOVER) or OR (DISCOVER_UNION) the unit's support words; the
+//     heads of the row add (error heads, newly selected blocks) through LDS
+//     and one wave updates the row's tag and the density counters.  Only a
+//     row split over several workgroups needs a device-scope atomic (an
+//     arrival word per row; the last workgroup to arrive does the update).
+// Cross-lane exchanges within 16 lanes use DPP; every load that does not
+// depend on arithmetic (partials, tile stats, old support words) is issued
+// before any of it.
 #include "wise_internal.h"
 
 namespace wise {
@@ -32,96 +36,170 @@ namespace {
 
 constexpr int kLanes = 64;
 constexpr int kUnroll = 8;
+constexpr int kHeadsPerGroup = 16;  // waves (heads) per finish workgroup
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-__device__ __forceinline__ int wave_sum_int(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-__device__ __forceinline__ double wave_inclusive_scan(double x, int lane) {
-#pragma unroll
-  for (int d = 1; d < kLanes; d <<= 1) {
-    const double y = __shfl_up(x, d);
-    if (lane >= d) x += y;
+// DPP controls: quad_perm [1,0,3,2] and [2,3,0,1]; row_shr:n (lane i reads
+// lane i-n of its 16-lane row, 0 where that leaves the row); row_ror:n (lane
+// i reads lane (i-n) mod 16 of its row).
+constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128, kRowRor12 = 0x12C;
+
+// Value held by lane (lane ^ M).
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
+  if constexpr (M == 1) {
+    return dpp32<kQuadSwap1>(x);
+  } else if constexpr (M == 2) {
+    return dpp32<kQuadSwap2>(x);
+  } else if constexpr (M == 4) {
+    const uint32_t down = dpp32<kRowRor4>(x), up = dpp32<kRowRor12>(x);
+    return (lane & 4) ? down : up;
+  } else if constexpr (M == 8) {
+    return dpp32<kRowRor8>(x);
+  } else {
+    return static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), M));
   }
-  return x;
 }
-__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long x, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), m);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), m);
+template <int M>
+__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long x, int lane) {
+  const uint32_t lo = xor_lane<M>(static_cast<uint32_t>(x), lane);
+  const uint32_t hi = xor_lane<M>(static_cast<uint32_t>(x >> 32), lane);
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
+
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+// All-lane reductions: rotations within each 16-lane row, then the four row
+// results combined in a fixed order (every lane returns the same bits).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, __uint_as_float(dpp32<kRowRor8>(__float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp32<kRowRor4>(__float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp32<kRowRor2>(__float_as_uint(x))));
+  x = fmaxf(x, __uint_as_float(dpp32<kRowRor1>(__float_as_uint(x))));
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += __uint_as_float(dpp32<kRowRor8>(__float_as_uint(x)));
+  x += __uint_as_float(dpp32<kRowRor4>(__float_as_uint(x)));
+  x += __uint_as_float(dpp32<kRowRor2>(__float_as_uint(x)));
+  x += __uint_as_float(dpp32<kRowRor1>(__float_as_uint(x)));
+  return ((lane_f(x, 0) + lane_f(x, 16)) + lane_f(x, 32)) + lane_f(x, 48);
+}
+__device__ __forceinline__ int wave_sum_int(int x) {
+  x += static_cast<int>(dpp32<kRowRor8>(static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp32<kRowRor4>(static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp32<kRowRor2>(static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp32<kRowRor1>(static_cast<uint32_t>(x)));
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double x) {
+  const unsigned long long b = static_cast<unsigned long long>(__double_as_longlong(x));
+  const uint32_t lo = dpp32<CTRL>(static_cast<uint32_t>(b));
+  const uint32_t hi = dpp32<CTRL>(static_cast<uint32_t>(b >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+__device__ __forceinline__ double lane_d(double x, int l) {
+  const unsigned long long b = static_cast<unsigned long long>(__double_as_longlong(x));
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(b), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), l);
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+// Exclusive prefix sum over lanes 0..lane-1: a shift scan within each
+// 16-lane row, then the totals of the lower rows added in row order.
+__device__ __forceinline__ double wave_exclusive_scan(double x, int lane) {
+  double s = x;
+  s += dpp64<kRowShr1>(s);
+  s += dpp64<kRowShr2>(s);
+  s += dpp64<kRowShr4>(s);
+  s += dpp64<kRowShr8>(s);
+  const double t0 = lane_d(s, 15), t1 = lane_d(s, 31), t2 = lane_d(s, 47);
+  const int row = lane >> 4;
+  double off = 0.0;
+  if (row >= 1) off += t0;
+  if (row >= 2) off += t1;
+  if (row >= 3) off += t2;
+  return (s - x) + off;
+}
+
 __device__ __forceinline__ float key_mass(unsigned long long key) {
   return __uint_as_float(static_cast<uint32_t>(key >> 32));
 }
 
-// Block masses of one discovery unit from its tile stats (loaded by the
-// caller, lane l holding blocks l*KPL .. l*KPL+KPL-1), sorted descending by
-// (mass, ~block index) with a bitonic network held in registers; the fp64
-// running sum picks K; the selected blocks' bits are ORed into s_bits.
-template <int KPL>
+// LDS written by some lanes of a wave and then read by other lanes of it.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One compare-exchange of the bitonic network between lanes lane and lane^LM.
+template <int LM>
+__device__ __forceinline__ unsigned long long bitonic_lanes(unsigned long long a, int lane, bool desc) {
+  const unsigned long long b = xor_lane64<LM>(a, lane);
+  const unsigned long long hi = a > b ? a : b, lo = a > b ? b : a;
+  return (((lane & LM) == 0) == desc) ? hi : lo;
+}
+
+// The bitonic network over positions e = lane*KPL + j, descending keys;
+// every step a compile-time (size, stride) pair.  The direction of position
+// e within a merge of `SIZE` is bit SIZE of e: of j while SIZE < KPL, of
+// lane*KPL otherwise.
+template <int KPL, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_merge(unsigned long long (&key)[KPL], int lane, bool desc_lane) {
+  if constexpr (STRIDE < KPL) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (j & STRIDE) continue;
+      const bool desc = SIZE < KPL ? (j & SIZE) == 0 : desc_lane;
+      const unsigned long long a = key[j], b = key[j | STRIDE];
+      const bool swap = (a < b) == desc;
+      key[j] = swap ? b : a;
+      key[j | STRIDE] = swap ? a : b;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) key[j] = bitonic_lanes<STRIDE / KPL>(key[j], lane, desc_lane);
+  }
+  if constexpr (STRIDE > 1) bitonic_merge<KPL, SIZE, STRIDE / 2>(key, lane, desc_lane);
+}
+template <int KPL, int SIZE, int NPOS>
+__device__ __forceinline__ void bitonic_sort(unsigned long long (&key)[KPL], int lane) {
+  bitonic_merge<KPL, SIZE, SIZE / 2>(key, lane, ((lane * KPL) & SIZE) == 0);
+  if constexpr (SIZE < NPOS) bitonic_sort<KPL, 2 * SIZE, NPOS>(key, lane);
+}
+
+// Eta selection of one discovery unit.  st[j] holds the tile stats (m_b,
+// l_b) of block b = lane*KPL + j.  Keys (mass bits, ~b) are sorted descending over
+// NPOS positions (NPOS >= nb, a power of two; positions beyond it belong to
+// independent copies of the network holding only padding), the fp64 running
+// sum picks K, and the selected blocks' bits are ORed into s_bits.
+template <int KPL, int NPOS>
 __device__ __forceinline__ int select_eta(const float2 (&st)[KPL], float eta, int nb, float M, float L, int lane,
                                           uint32_t *s_bits) {
-  unsigned long long key[KPL];
   const float invL = 1.0f / L;
+  unsigned long long key[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int b = lane * KPL + j;
-    key[j] = 0ull;  // padding sorts after every block
-    if (b < nb) {
-      const float mass = st[j].y * __builtin_amdgcn_exp2f(st[j].x - M) * invL;
-      key[j] = (static_cast<unsigned long long>(__float_as_uint(mass)) << 32) |
-               static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(b));
-    }
+    const float mass = st[j].y * __builtin_amdgcn_exp2f(st[j].x - M) * invL;
+    key[j] = b < nb ? (static_cast<unsigned long long>(__float_as_uint(mass)) << 32) |
+                          static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(b))
+                    : 0ull;  // padding sorts after every block
   }
-  // bitonic network over positions e = lane*KPL + j, descending keys
-  constexpr int N = kLanes * KPL;
-#pragma unroll
-  for (int size = 2; size <= N; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride < KPL) {
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          if (j & stride) continue;
-          const int e = lane * KPL + j;
-          const bool desc = (e & size) == 0;
-          const unsigned long long a = key[j], b = key[j | stride];
-          const bool swap = (a < b) == desc;
-          key[j] = swap ? b : a;
-          key[j | stride] = swap ? a : b;
-        }
-      } else {
-        const int lm = stride / KPL;
-        const bool lower = (lane & lm) == 0;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const int e = lane * KPL + j;
-          const bool desc = (e & size) == 0;
-          const unsigned long long a = key[j], b = shfl_xor64(a, lm);
-          const unsigned long long hi = a > b ? a : b, lo = a > b ? b : a;
-          key[j] = (lower == desc) ? hi : lo;
-        }
-      }
-    }
-  }
-  // fp64 running sum in sorted order
+  bitonic_sort<KPL, 2, NPOS>(key, lane);
+  // fp64 running sum in sorted order: each lane's own run, then the lanes below
   double part = 0.0;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) part += static_cast<double>(key_mass(key[j]));
-  const double incl = wave_inclusive_scan(part, lane);
-  const double prev = __shfl_up(incl, 1);
-  double run = lane ? prev : 0.0;
+  double run = wave_exclusive_scan(part, lane);
   int kfound = nb;
   bool hit = false;
 #pragma unroll
@@ -150,13 +228,17 @@ struct UnitInfo {
   bool row_bad;
 };
 
-// Finish of one unit.  Every load that does not depend on arithmetic (item
-// partials, tile stats, old support words) is issued up front, so the
-// discovery path waits on memory about once instead of once per step.
-template <int KPL>
-__device__ __forceinline__ void finish_unit(const FinishParams &p, const UnitInfo &ui, float *s_w,
-                                            uint32_t *s_bits) {
-  const int lane = threadIdx.x;
+struct UnitResult {
+  bool err;      // the unit read a bad page (its output is NaN)
+  int selected;  // blocks this unit newly selected
+};
+
+// Finish of one unit by one wave.  No workgroup barrier in here: the waves
+// of a workgroup take different paths through it.
+template <int KPL, int NPOS>
+__device__ __forceinline__ UnitResult finish_unit(const FinishParams &p, const UnitInfo &ui, float *s_w,
+                                                  uint32_t *s_bits) {
+  const int lane = threadIdx.x & (kLanes - 1);
   const int items = ui.items;
   const int64_t base = static_cast<int64_t>(ui.u) * p.items_per_unit;
   const int D = p.head_dim;
@@ -214,7 +296,7 @@ __device__ __forceinline__ void finish_unit(const FinishParams &p, const UnitInf
   const float L = wave_sum(Lp);
   if (discover)
     for (int w = lane; w < kMaxWords; w += kLanes) s_bits[w] = 0u;
-  __syncthreads();
+  wave_lds_sync();
 #pragma unroll
   for (int q = 0; q < kDims; ++q) {
     const int dd = lane + q * kLanes;
@@ -235,44 +317,46 @@ __device__ __forceinline__ void finish_unit(const FinishParams &p, const UnitInf
   }
   if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
 
-  if (!stateful) return;
-  const int slot = ui.slot;
-  wise_tag *tag = p.tags + static_cast<int64_t>(slot) * p.layers + p.layer;
-  if (!discover) {
-    // a union row whose discovery window is broken ran dense: the rest of
-    // this token runs dense too
-    if (ui.req == WISE_DISCOVER_UNION && ui.h == 0 && lane == 0) tag->discoveries = 0;
-    return;
-  }
+  UnitResult res{err, 0};
+  if (!discover || err) return res;
 
   // ---- 2. eta selection, 3. support write / union ----
-  int selected = 0;
-  if (!err) {
-    const int K = select_eta<KPL>(st, p.eta, ui.nb, M, L, lane, s_bits);
-    __syncthreads();
-    int added = 0;
-    for (int w = lane; w < p.words; w += kLanes) {
-      const uint32_t nw = w < kMaxWords ? s_bits[w] : 0u;
-      if (ui.eff == WISE_DISCOVER) {
-        sw[w] = nw;
-      } else {
-        const uint32_t old = w == lane ? old_word : sw[w];
-        sw[w] = old | nw;
-        added += __popc(nw & ~old);
-      }
+  const int K = select_eta<KPL, NPOS>(st, p.eta, ui.nb, M, L, lane, s_bits);
+  wave_lds_sync();
+  int added = 0;
+  for (int w = lane; w < p.words; w += kLanes) {
+    const uint32_t nw = w < kMaxWords ? s_bits[w] : 0u;
+    if (ui.eff == WISE_DISCOVER) {
+      sw[w] = nw;
+    } else {
+      const uint32_t old = w == lane ? old_word : sw[w];
+      sw[w] = old | nw;
+      added += __popc(nw & ~old);
     }
-    selected = ui.eff == WISE_DISCOVER ? K : wave_sum_int(added);
   }
+  res.selected = ui.eff == WISE_DISCOVER ? K : wave_sum_int(added);
+  return res;
+}
 
-  // ---- the row's tag and density counts: by the last of its heads to arrive ----
-  if (lane != 0) return;
-  const unsigned long long mine =
-      1ull | (err ? (1ull << 16) : 0ull) | (static_cast<unsigned long long>(selected) << 32);
-  const unsigned long long all = atomicAdd(p.row_done + ui.r, mine) + mine;
-  if (static_cast<int>(all & 0xFFFFull) != p.heads) return;
-  const int err_heads = static_cast<int>((all >> 16) & 0xFFFFull);
+// The smallest sort size holding the unit's nb blocks, up to KMAX per lane.
+template <int KPL, int KMAX>
+__device__ __forceinline__ UnitResult finish_sized(const FinishParams &p, const UnitInfo &ui, float *s_w,
+                                                   uint32_t *s_bits) {
+  if constexpr (KPL >= KMAX) {
+    return finish_unit<KMAX, KMAX * kLanes>(p, ui, s_w, s_bits);
+  } else {
+    if (ui.nb <= KPL * kLanes) return finish_unit<KPL, KPL * kLanes>(p, ui, s_w, s_bits);
+    return finish_sized<2 * KPL, KMAX>(p, ui, s_w, s_bits);
+  }
+}
+
+// Tag and density counters of a discovery row once all of its heads are
+// done: err_heads of them read a bad page, `selected` blocks were newly set.
+__device__ __forceinline__ void row_bookkeeping(const FinishParams &p, const UnitInfo &ui, int err_heads,
+                                                unsigned long long selected) {
+  wise_tag *tag = p.tags + static_cast<int64_t>(ui.slot) * p.layers + p.layer;
   if (p.counters) {
-    atomicAdd(p.counters + WISE_CTR_SELECTED, all >> 32);
+    atomicAdd(p.counters + WISE_CTR_SELECTED, selected);
     if (ui.eff == WISE_DISCOVER)
       atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(ui.nb) * (p.heads - err_heads));
   }
@@ -286,13 +370,26 @@ __device__ __forceinline__ void finish_unit(const FinishParams &p, const UnitInf
   }
 }
 
-__global__ __launch_bounds__(kLanes) void finish_kernel(const FinishParams p) {
-  __shared__ float s_w[kMaxItemsPerUnit];
-  __shared__ uint32_t s_bits[kMaxWords];
+// Waves per workgroup for units of up to 64*KMAX blocks: 16 (a row of up to
+// 16 heads in one workgroup) while a wave fits 128 registers, else 4.
+constexpr int waves_for(int kmax) { return kmax <= 16 ? kHeadsPerGroup : 4; }
+
+template <int KMAX>
+__global__ __launch_bounds__(kLanes *waves_for(KMAX)) void finish_kernel(const FinishParams p, int waves,
+                                                                         int groups) {
+  __shared__ float s_w[kHeadsPerGroup][kMaxItemsPerUnit];
+  __shared__ uint32_t s_bits[kHeadsPerGroup][kMaxWords];
+  __shared__ int s_err[kHeadsPerGroup];
+  __shared__ int s_sel[kHeadsPerGroup];
+
+  const int lane = threadIdx.x & (kLanes - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   UnitInfo ui;
-  ui.u = blockIdx.x;
-  ui.r = ui.u / p.heads;
-  ui.h = ui.u - ui.r * p.heads;
+  ui.r = blockIdx.x / groups;
+  const int g = blockIdx.x - ui.r * groups;
+  ui.h = g * waves + wave;
+  const bool active = ui.h < p.heads;
+  ui.u = ui.r * p.heads + (active ? ui.h : 0);
   // independent scalar loads, issued together
   const int code = p.row_code[ui.r];
   const int items = p.unit_items[ui.u];
@@ -304,19 +401,72 @@ __global__ __launch_bounds__(kLanes) void finish_kernel(const FinishParams p) {
   ui.items = ui.row_bad ? 0 : items;
   ui.nb = ui.row_bad ? 0 : (n + kBlock - 1) / kBlock;
   ui.slot = slot;
-  if (ui.nb <= kLanes) finish_unit<1>(p, ui, s_w, s_bits);
-  else if (ui.nb <= 2 * kLanes) finish_unit<2>(p, ui, s_w, s_bits);
-  else if (ui.nb <= 4 * kLanes) finish_unit<4>(p, ui, s_w, s_bits);
-  else if (ui.nb <= 8 * kLanes) finish_unit<8>(p, ui, s_w, s_bits);
-  else if (ui.nb <= 16 * kLanes) finish_unit<16>(p, ui, s_w, s_bits);
-  else finish_unit<32>(p, ui, s_w, s_bits);
+
+  UnitResult res{false, 0};
+  if (active) {
+    float *sw = s_w[wave];
+    uint32_t *sb = s_bits[wave];
+    if (ui.nb <= 16) res = finish_unit<1, 16>(p, ui, sw, sb);
+    else if (ui.nb <= 32) res = finish_unit<1, 32>(p, ui, sw, sb);
+    else res = finish_sized<1, KMAX>(p, ui, sw, sb);
+  }
+  if (lane == 0) {
+    s_err[wave] = res.err ? 1 : 0;
+    s_sel[wave] = res.selected;
+  }
+  __syncthreads();  // reached once by every wave of the workgroup
+
+  const bool stateful = p.support != nullptr && !ui.row_bad && ui.req != WISE_DENSE;
+  if (!stateful || wave != 0 || lane != 0) return;
+  if (ui.eff != WISE_DISCOVER && ui.eff != WISE_DISCOVER_UNION) {
+    // a union row whose discovery window is broken ran dense: the rest of
+    // this token runs dense too
+    if (ui.req == WISE_DISCOVER_UNION && g == 0)
+      p.tags[static_cast<int64_t>(ui.slot) * p.layers + p.layer].discoveries = 0;
+    return;
+  }
+  int err_heads = 0;
+  unsigned long long selected = 0ull;
+  for (int w = 0; w < waves; ++w) {
+    err_heads += s_err[w];
+    selected += static_cast<unsigned long long>(s_sel[w]);
+  }
+  if (groups == 1) {
+    row_bookkeeping(p, ui, err_heads, selected);
+    return;
+  }
+  // the row spans several workgroups: the last one to arrive does it
+  const unsigned long long mine = 1ull | (static_cast<unsigned long long>(err_heads) << 16) | (selected << 32);
+  const unsigned long long all = atomicAdd(p.row_done + ui.r, mine) + mine;
+  if (static_cast<int>(all & 0xFFFFull) != groups) return;
+  row_bookkeeping(p, ui, static_cast<int>((all >> 16) & 0xFFFFull), all >> 32);
 }
 
 }  // namespace
 
-hipError_t launch_finish(const FinishParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL(finish_kernel, dim3(static_cast<unsigned>(p.rows) * p.heads), dim3(kLanes), 0, stream, p);
+namespace {
+template <int KMAX>
+hipError_t launch_finish_typed(const FinishParams &p, hipStream_t stream) {
+  constexpr int kWaves = waves_for(KMAX);
+  const int waves = p.heads < kWaves ? p.heads : kWaves;
+  const int groups = (p.heads + waves - 1) / waves;
+  hipLaunchKernelGGL(finish_kernel<KMAX>, dim3(static_cast<unsigned>(p.rows) * groups), dim3(kLanes * waves), 0,
+                     stream, p, waves, groups);
   return hipGetLastError();
+}
+}  // namespace
+
+// The kernel is specialised on the largest unit the call can hold (from the
+// host-known block bound), so short contexts do not pay for the registers
+// of long ones.
+hipError_t launch_finish(const FinishParams &p, hipStream_t stream) {
+  const int nb = p.max_blocks;
+  if (nb <= kLanes) return launch_finish_typed<1>(p, stream);
+  if (nb <= 2 * kLanes) return launch_finish_typed<2>(p, stream);
+  if (nb <= 4 * kLanes) return launch_finish_typed<4>(p, stream);
+  if (nb <= 8 * kLanes) return launch_finish_typed<8>(p, stream);
+  if (nb <= 16 * kLanes) return launch_finish_typed<16>(p, stream);
+  return launch_finish_typed<32>(p, stream);
 }
 
 }  // namespace wise
