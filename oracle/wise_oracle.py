@@ -31,7 +31,12 @@ Where the page is silent, this oracle takes these readings:
   * the support is the shortest such prefix whose running fp64 sum reaches
     (>=) eta; at least one block; all blocks if rounding never reaches eta;
   * sparse attention renormalises within the support (masked attention);
-  * tags count recorded discovery depths; see ``plan_row``.
+  * tags count recorded discovery depths; see ``plan_row``;
+  * the page's second discovery route (rebuild block mass from a dense
+    kernel's LSE, rereading K) takes lse = log sum_t exp(s_t) in natural-log
+    units over the row's whole context; a block's mass is then the sum of
+    exp(s_t - lse) over its tokens, selection as above; a non-finite lse is a
+    data error of its unit.
 
 Every function here has a pin in ``tests/test_oracle_pins.py``.
 """
@@ -268,7 +273,8 @@ class UnitResult:
 
 @dataclasses.dataclass
 class CallResult:
-    out: np.ndarray                          # [R, H, d] fp64 (NaN for error units)
+    out: Optional[np.ndarray]                # [R, H, d] fp64 (NaN for error units); None
+                                             # for the LSE route, which makes no output
     support: np.ndarray                      # updated copy
     tags: np.ndarray                         # updated copy
     counters: np.ndarray                     # delta: fallback, selected, causal, errors
@@ -366,6 +372,92 @@ def run_call(*, q, k_cache, v_cache, block_table, ctx_len, page_size: int, num_p
             tg[slot, layer] = update_tag(tg[slot, layer], req, eff, int(row_request[r]),
                                          int(row_position[r]), row_err)
     return CallResult(out, sup, tg, counters, eff_all, units)
+
+
+# ----------------------------------------------------------------------------
+# O9 discovery after an external dense kernel: the page's FlashAttention
+#    route ("What changes", second bullet) rereads K once and rebuilds every
+#    block's mass from the log-sum-exp the dense kernel reported.  With
+#    lse = log sum_t exp(s_t), the mass of block b is sum over its tokens of
+#    exp(s_t - lse), i.e. its share of the row's softmax.
+# ----------------------------------------------------------------------------
+
+def row_lse(s: np.ndarray) -> float:
+    """log sum_t exp(s_t) of one row's scores (what a dense kernel reports)."""
+    M = float(np.max(s))
+    return M + float(np.log(np.exp(s - M).sum()))
+
+
+def lse_block_mass(s: np.ndarray, lse: float) -> np.ndarray:
+    """Per block b: sum over the block's valid tokens of exp(s_t - lse)."""
+    n = len(s)
+    return np.array([np.exp(s[b * BLOCK: min(n, b * BLOCK + BLOCK)] - lse).sum()
+                     for b in range(num_blocks(n))])
+
+
+def run_lse_call(*, q, k_cache, block_table, ctx_len, page_size: int, num_pages: int,
+                 max_ctx: int, lse, union: bool, support: np.ndarray, tags: np.ndarray,
+                 scale: float = 0.0, layer: int = 0,
+                 slot_of_row: Optional[Sequence[int]] = None,
+                 row_request: Optional[Sequence[int]] = None,
+                 row_position: Optional[Sequence[int]] = None, eta: float = 0.95,
+                 rows: Optional[Sequence[int]] = None) -> CallResult:
+    """One discovery depth by the LSE route, every row DISCOVER (or
+    DISCOVER_UNION when ``union``).  ``lse`` [R, H] is the dense kernel's
+    log-sum-exp of the scaled scores.  No attention output is produced (the
+    dense kernel made it); selection, support, tags and counters follow
+    ``run_call``.  A non-finite lse, like a bad page, is a data error of its
+    (row, head) unit and breaks the row's discovery window.
+    """
+    R, H, d = q.shape
+    scale = scale if scale else default_scale(d)
+    sup, tg = support.copy(), tags.copy()
+    counters = np.zeros(4, dtype=np.int64)
+    eff_all = np.full(R, -1, dtype=np.int64)
+    units = {}
+    slots, words = sup.shape[0], sup.shape[3]
+    req = DISCOVER_UNION if union else DISCOVER
+    for r in (range(R) if rows is None else rows):
+        n = int(ctx_len[r])
+        slot = r if slot_of_row is None else int(slot_of_row[r])
+        if not (1 <= n <= max_ctx) or not (0 <= slot < slots):
+            counters[3] += H
+            continue
+        nb = num_blocks(n)
+        eff, fb = plan_row(req, tg[slot, layer], int(row_request[r]), int(row_position[r]), 1)
+        counters[0] += int(fb)
+        eff_all[r] = eff
+        row_err = False
+        if eff != DENSE:
+            qf = widen(q[r])
+            toks = np.arange(n)
+            pages = np.asarray(block_table[r])[toks // page_size]
+            page_bad = bool(np.any((pages < 0) | (pages >= num_pages)))
+            for h in range(H):
+                lse_rh = float(lse[r][h])
+                if page_bad or not np.isfinite(lse_rh):
+                    counters[3] += 1
+                    row_err = True
+                    units[(r, h)] = UnitResult(None, True, eff, np.arange(nb))
+                    continue
+                s = scale * (gather_tokens(k_cache, block_table[r], toks, page_size, h) @ qf[h])
+                m, l = tile_stats(s)
+                p = lse_block_mass(s, lse_rh)
+                sel = eta_select(p, eta)
+                new = blocks_to_bits(sel.blocks, words)
+                old = sup[slot, layer, h].copy()
+                if eff == DISCOVER:
+                    sup[slot, layer, h] = new
+                    counters[1] += sel.K
+                    counters[2] += nb
+                else:
+                    sup[slot, layer, h] = old | new
+                    counters[1] += int(sum(bin(int(x)).count("1") for x in (new & ~old)))
+                units[(r, h)] = UnitResult(None, False, eff, np.arange(nb), m=m, l=l, mass=p,
+                                           selection=sel)
+        tg[slot, layer] = update_tag(tg[slot, layer], req, eff, int(row_request[r]),
+                                     int(row_position[r]), row_err)
+    return CallResult(None, sup, tg, counters, eff_all, units)
 
 
 def density(counters: Sequence[int]) -> float:

@@ -391,6 +391,86 @@ def test_synth_encodings_and_layout():
     assert ctx.min() >= 512 and ctx.max() <= 32768
 
 
+# ----------------------------------------------------------------------------- O9 LSE route
+
+def brute_lse(s):
+    mx = max(s)
+    return mx + math.log(math.fsum(math.exp(x - mx) for x in s))
+
+
+@pytest.mark.parametrize("n", [1, 32, 33, 95, 200])
+def test_lse_block_mass_is_softmax_block_sums(n):
+    """Block masses rebuilt from the row's log-sum-exp are the block sums of
+    the brute-force softmax; a larger lse scales them by exp(-delta)."""
+    rng = np.random.default_rng(500 + n)
+    q, K, V = rand_qkv(rng, n, 4)
+    _, probs = brute_softmax_attention(q.tolist(), K.tolist(), V.tolist(), 0.8)
+    s_py = [0.8 * math.fsum(q[i] * K[t][i] for i in range(4)) for t in range(n)]
+    lse = brute_lse(s_py)
+    s = 0.8 * (K @ q)
+    assert O.row_lse(s) == pytest.approx(lse, abs=1e-12)
+    nb = (n + 31) // 32
+    brute = np.array([math.fsum(probs[32 * b: min(n, 32 * b + 32)]) for b in range(nb)])
+    p = O.lse_block_mass(s, lse)
+    assert len(p) == nb
+    np.testing.assert_allclose(p, brute, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(O.lse_block_mass(s, lse + 0.25), brute * math.exp(-0.25), rtol=1e-13)
+
+
+def test_lse_block_mass_closed_form():
+    """Equal scores c over n tokens: lse = c + ln n and each block holds its
+    token count over n (the partial last block included)."""
+    n = 75
+    s = np.full(n, 1.7)
+    assert O.row_lse(s) == pytest.approx(1.7 + math.log(n), abs=1e-14)
+    np.testing.assert_allclose(O.lse_block_mass(s, 1.7 + math.log(n)), [32 / n, 32 / n, 11 / n],
+                               rtol=1e-14)
+
+
+def test_lse_call_matches_tile_route_and_unions():
+    """The LSE route picks the supports, tags and counts that discovery from
+    the tile stats picks; a second LSE depth ORs like DISCOVER_UNION; a union
+    without a window falls back; a non-finite lse is a data error."""
+    rng = np.random.default_rng(21)
+    case, Kl, Vl = paged_case(rng, 150, H=2)
+    sup, tags = state(heads=2)
+    common = dict(layer=0, row_request=[7], row_position=[42], eta=0.9)
+    lse = np.array([[brute_lse((case["q"][0, h].astype(float) @ Kl[h].astype(float).T
+                                / math.sqrt(8)).tolist()) for h in range(2)]])
+    kw = {k: case[k] for k in ("q", "k_cache", "block_table", "ctx_len", "page_size", "num_pages",
+                               "max_ctx")}
+    ref = O.run_call(**case, modes=[O.DISCOVER], support=sup, tags=tags, required=1, **common)
+    got = O.run_lse_call(**kw, lse=lse, union=False, support=sup, tags=tags, **common)
+    assert got.out is None
+    for h in range(2):
+        assert not ref.units[(0, h)].selection.near_eta(0.9)
+        np.testing.assert_allclose(got.units[(0, h)].mass, ref.units[(0, h)].mass, atol=1e-14)
+    assert np.array_equal(got.support, ref.support)
+    assert got.tags.tobytes() == ref.tags.tobytes()
+    assert got.counters.tolist() == ref.counters.tolist()
+    # second discovery depth with fresh queries: the LSE union equals the tile-stat union
+    case2 = dict(case)
+    case2["q"] = rng.standard_normal(case["q"].shape).astype(np.float32)
+    kw2 = dict(kw, q=case2["q"])
+    lse2 = np.array([[brute_lse((case2["q"][0, h].astype(float) @ Kl[h].astype(float).T
+                                 / math.sqrt(8)).tolist()) for h in range(2)]])
+    ref_u = O.run_call(**case2, modes=[O.DISCOVER_UNION], support=ref.support, tags=ref.tags,
+                       required=1, **common)
+    got_u = O.run_lse_call(**kw2, lse=lse2, union=True, support=got.support, tags=got.tags, **common)
+    assert np.array_equal(got_u.support, ref_u.support)
+    assert got_u.tags[0, 0]["discoveries"] == 2 and got_u.counters.tolist() == ref_u.counters.tolist()
+    # a union with no window: dense fallback, window invalidated, support untouched
+    fb = O.run_lse_call(**kw2, lse=lse2, union=True, support=sup, tags=tags, **common)
+    assert fb.counters.tolist() == [1, 0, 0, 0]
+    assert fb.tags[0, 0]["discoveries"] == 0 and np.array_equal(fb.support, sup)
+    # a non-finite lse: one error, the window breaks
+    bad = lse.copy()
+    bad[0, 1] = np.nan
+    e = O.run_lse_call(**kw, lse=bad, union=False, support=sup, tags=tags, **common)
+    assert e.counters[3] == 1 and e.tags[0, 0]["discoveries"] == 0
+    assert np.array_equal(e.support[0, 0, 0], ref.support[0, 0, 0])
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def test_pins_catch_planted_mistakes(monkeypatch):
@@ -417,15 +497,26 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         m, l = real_stats(np.concatenate([s, np.zeros((-len(s)) % 32)]))
         return m, l
 
+    real_lse_mass = O.lse_block_mass
+
+    def lse_sign(s, lse):                       # exp(s + lse) instead of exp(s - lse)
+        return real_lse_mass(s, -lse)
+
+    def lse_full_blocks(s, lse):                # the partial last block dropped
+        return real_lse_mass(s[: 32 * (len(s) // 32)] if len(s) >= 32 else s, lse)
+
     planted = [
         ("eta_select", strict_cut, lambda: test_selection_dominant_and_single_block()),
         ("eta_select", index_desc, lambda: test_selection_tie_break_equal_masses()),
         ("block_mass", no_norm, lambda: test_tile_stats_and_mass(95)),
         ("tile_stats", last_tile_full, lambda: test_tile_stats_and_mass(33)),
+        ("lse_block_mass", lse_sign, lambda: test_lse_block_mass_is_softmax_block_sums(95)),
+        ("lse_block_mass", lse_full_blocks, lambda: test_lse_block_mass_closed_form()),
     ]
+    reals = {"eta_select": real_select, "block_mass": real_mass, "tile_stats": real_stats,
+             "lse_block_mass": real_lse_mass}
     for name, fn, pin in planted:
         monkeypatch.setattr(O, name, fn)
         with pytest.raises(AssertionError):
             pin()
-        monkeypatch.setattr(O, name, {"eta_select": real_select, "block_mass": real_mass,
-                                      "tile_stats": real_stats}[name])
+        monkeypatch.setattr(O, name, reals[name])
