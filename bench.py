@@ -33,6 +33,7 @@ from block_sparse_paged_split_amd import wise as W  # noqa: E402
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MODE_NAME = {W.WISE_DENSE: "dense", W.WISE_DISCOVER: "discover",
              W.WISE_DISCOVER_UNION: "discover_union", W.WISE_SPARSE: "sparse"}
+LSE_ROUTE = -1  # split_bytes key of discovery by the LSE route
 
 
 def log(*a):
@@ -64,11 +65,33 @@ def split_bytes(w, ctx, eff_modes, support_words):
             for blk in np.nonzero(bits.any(axis=0))[0]:
                 pages.update(range((32 * blk) // P, (min(n, 32 * blk + 32) - 1) // P + 1))
             total += int(2 * toks.sum() * d * e) + H * d * e + H * 4 * ((nb + 31) // 32) + 4 * len(pages)
+        elif mode == LSE_ROUTE:
+            # discovery by the LSE route: K only, q, the tile stats written
+            total += H * (n * d * e + d * e + 8 * nb) + 4 * ((n + P - 1) // P)
         else:
             total += H * (2 * n * d * e + d * e) + 4 * ((n + P - 1) // P)
             if mode != W.WISE_DENSE:
                 total += H * 8 * nb
     return total
+
+
+def external_lse(layer_dev, ctx, page_size, scale=None):
+    """[R, H] fp32 log-sum-exp of every (row, head)'s scaled scores, computed
+    with plain torch ops from the paged cache: the stand-in for the external
+    dense kernel whose LSE the LSE route consumes (untimed setup)."""
+    import torch
+    q, k, bt = layer_dev.q, layer_dev.k, layer_dev.block_table
+    R, H, d = q.shape
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    out = torch.empty((R, H), dtype=torch.float32, device=q.device)
+    for r in range(R):
+        n = int(ctx[r])
+        t = torch.arange(n, device=q.device)
+        pages = bt[r, t // page_size].long()
+        K = k[pages, :, t % page_size, :].float()                  # [n, H, d]
+        s = (K * q[r].float()[None]).sum(dim=-1).t() * scale        # [H, n]
+        out[r] = torch.logsumexp(s, dim=1)
+    return out
 
 
 def cpu_baseline(w, min_s=10.0, max_rows=32):
@@ -208,6 +231,8 @@ def main():
                     help="distinct KV sets per depth for multi-layer workloads, rotated over the layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-reference", action="store_true")
+    ap.add_argument("--no-lse-route", action="store_true",
+                    help="skip the timing of discovery by the LSE route")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (for counter-collection runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -343,6 +368,38 @@ def main():
             modes_out["dense_same_kv"] = {"split_us": round(dms * 1e3, 2), "algorithmic_MB": round(dbytes / 1e6, 3),
                                           "GBps": round(dbytes / (dms * 1e-3) / 1e9, 1)}
             modes_out[key]["speedup_vs_dense"] = round(dms * 1e3 / modes_out[key]["split_us"], 3)
+
+    # ---- discovery by the LSE route (K reread, no output), rotating over every KV set ----
+    if not args.no_lse_route and not plan.mixed:
+        sets = []
+        for key, layer_dev in plan.kv.items():
+            a = layer_dev.attn()
+            lse = external_lse(layer_dev, plan.ctx, w.page_size)
+            sets.append((a, lse))
+        s = plan.state.view(0, 1, w.eta)
+        n_it = 4 * len(sets)
+        ev3 = harness.HipEvents(2 * n_it + 2)
+        for a, lse in sets[:2]:
+            W.wise_discover_lse(a, s, False, int(lse.data_ptr()), plan.ws.ptr, plan.ws.nbytes, sh)
+        ev3.record(2 * n_it, sh)
+        for it in range(n_it):       # back to back, like the timed steps
+            a, lse = sets[it % len(sets)]
+            a.ev_split_begin, a.ev_split_end = ev3.handle(2 * it), ev3.handle(2 * it + 1)
+            W.wise_discover_lse(a, s, False, int(lse.data_ptr()), plan.ws.ptr, plan.ws.nbytes, sh)
+        ev3.record(2 * n_it + 1, sh)
+        torch.cuda.synchronize()
+        split_ms = [ev3.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]
+        call_ms = [ev3.elapsed_ms(2 * n_it, 2 * n_it + 1) / n_it]
+        for a, _ in sets:
+            a.ev_split_begin = a.ev_split_end = None
+        lbytes = split_bytes(w, plan.ctx, np.full(w.rows, LSE_ROUTE), None)
+        sms = float(np.mean(split_ms))
+        modes_out["lse_discover"] = {"split_us": round(sms * 1e3, 2),
+                                     "call_us": round(float(np.mean(call_ms)) * 1e3, 2),
+                                     "algorithmic_MB": round(lbytes / 1e6, 3),
+                                     "GBps": round(lbytes / (sms * 1e-3) / 1e9, 1),
+                                     "note": "K-only split + LSE selection, eager back-to-back calls; "
+                                             "not part of a step"}
 
     rows_per_step = w.rows * calls
     out = {

@@ -65,15 +65,18 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
-wise_status check_attn(const wise_attn *a, Layout *L) {
+// k_only: the call reads q and K only (LSE route); v_cache and out may be NULL.
+wise_status check_attn(const wise_attn *a, Layout *L, bool k_only = false) {
   if (!a) return WISE_E_ARG;
   if (a->dtype != WISE_BF16 && a->dtype != WISE_F32) return WISE_E_UNSUPPORTED;
   if (a->head_dim != 64 && a->head_dim != 128) return WISE_E_UNSUPPORTED;
   if (a->rows < 1 || a->heads < 1 || a->max_ctx < 1 || a->num_pages < 1) return WISE_E_ARG;
   if (!is_pow2(a->page_size) || a->page_size < 8 || a->page_size > 4096) return WISE_E_UNSUPPORTED;
   if (a->max_ctx > kMaxCtx) return WISE_E_UNSUPPORTED;
-  if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->ctx_len || !a->out) return WISE_E_ARG;
-  if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->out, 16))
+  if (!a->q || !a->k_cache || !a->block_table || !a->ctx_len) return WISE_E_ARG;
+  if (!k_only && (!a->v_cache || !a->out)) return WISE_E_ARG;
+  if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || (a->v_cache && !aligned(a->v_cache, 16)) ||
+      (a->out && !aligned(a->out, 16)))
     return WISE_E_ARG;
   if (a->tile_stats && !aligned(a->tile_stats, 8)) return WISE_E_ARG;
   const int64_t e = a->dtype == WISE_BF16 ? 2 : 4;
@@ -134,9 +137,9 @@ int log2i(int x) {
 }
 
 wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, const uint8_t *row_mode,
-                   void *ws, size_t ws_bytes, void *stream) {
+                   void *ws, size_t ws_bytes, void *stream, bool k_only = false) {
   Layout L;
-  wise_status st = check_attn(a, &L);
+  wise_status st = check_attn(a, &L, k_only);
   if (st != WISE_OK) return st;
   const bool stateful = uniform_mode != WISE_DENSE || row_mode != nullptr;
   if (stateful) {
@@ -201,40 +204,16 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
   const bool listed = (row_mode != nullptr || uniform_mode == WISE_SPARSE) && p.chunk_groups > 1;
   const int cus = listed ? compute_units() : 0;
   if (listed && cus <= 0) return WISE_E_HIP;
-  if (launch_split(p, a->dtype, a->head_dim, listed, cus, static_cast<hipEvent_t>(a->ev_split_begin),
+  if (launch_split(p, a->dtype, a->head_dim, listed, k_only, cus, static_cast<hipEvent_t>(a->ev_split_begin),
                    static_cast<hipEvent_t>(a->ev_split_end), strm) != hipSuccess)
     return WISE_E_HIP;
   return WISE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t wise_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t max_ctx) {
+wise_status finish(const wise_attn *a, const wise_support *s, const float *lse, void *ws, size_t ws_bytes,
+                   void *stream) {
   Layout L;
-  return make_layout(rows, heads, head_dim, max_ctx, &L) ? L.total : 0;
-}
-
-wise_status wise_decode_dense(const wise_attn *a, void *ws, size_t ws_bytes, void *stream) {
-  return decode(a, nullptr, WISE_DENSE, nullptr, ws, ws_bytes, stream);
-}
-
-wise_status wise_decode_discover(const wise_attn *a, const wise_support *s, int32_t union_with_previous,
-                                 void *ws, size_t ws_bytes, void *stream) {
-  return decode(a, s, union_with_previous ? WISE_DISCOVER_UNION : WISE_DISCOVER, nullptr, ws, ws_bytes,
-                stream);
-}
-
-wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s, const uint8_t *row_mode, void *ws,
-                               size_t ws_bytes, void *stream) {
-  return decode(a, s, WISE_SPARSE, row_mode, ws, ws_bytes, stream);
-}
-
-wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws, size_t ws_bytes,
-                               void *stream) {
-  Layout L;
-  wise_status st = check_attn(a, &L);
+  wise_status st = check_attn(a, &L, lse != nullptr);
   if (st != WISE_OK) return st;
   if (s) {
     st = check_support(a, s, L);
@@ -270,8 +249,53 @@ wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *
     p.eta = s->eta;
     p.counters = reinterpret_cast<unsigned long long *>(s->counters);
   }
+  p.lse = lse;
   if (launch_finish(p, static_cast<hipStream_t>(stream)) != hipSuccess) return WISE_E_HIP;
   return WISE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wise_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t max_ctx) {
+  Layout L;
+  return make_layout(rows, heads, head_dim, max_ctx, &L) ? L.total : 0;
+}
+
+wise_status wise_decode_dense(const wise_attn *a, void *ws, size_t ws_bytes, void *stream) {
+  return decode(a, nullptr, WISE_DENSE, nullptr, ws, ws_bytes, stream);
+}
+
+wise_status wise_decode_discover(const wise_attn *a, const wise_support *s, int32_t union_with_previous,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  return decode(a, s, union_with_previous ? WISE_DISCOVER_UNION : WISE_DISCOVER, nullptr, ws, ws_bytes,
+                stream);
+}
+
+wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s, const uint8_t *row_mode, void *ws,
+                               size_t ws_bytes, void *stream) {
+  return decode(a, s, WISE_SPARSE, row_mode, ws, ws_bytes, stream);
+}
+
+wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws, size_t ws_bytes,
+                               void *stream) {
+  return finish(a, s, nullptr, ws, ws_bytes, stream);
+}
+
+wise_status wise_discover_lse(const wise_attn *a, const wise_support *s, int32_t union_with_previous,
+                              const float *lse, void *ws, size_t ws_bytes, void *stream) {
+  if (!s || !lse || !aligned(lse, 4)) return WISE_E_ARG;
+  // validate everything before the first launch, so an error enqueues nothing
+  Layout L;
+  wise_status st = check_attn(a, &L, true);
+  if (st == WISE_OK) st = check_support(a, s, L);
+  if (st == WISE_OK) st = check_ws(ws, ws_bytes, L);
+  if (st != WISE_OK) return st;
+  st = decode(a, s, union_with_previous ? WISE_DISCOVER_UNION : WISE_DISCOVER, nullptr, ws, ws_bytes, stream,
+              true);
+  if (st != WISE_OK) return st;
+  return finish(a, s, lse, ws, ws_bytes, stream);
 }
 
 const char *wise_status_string(wise_status st) {

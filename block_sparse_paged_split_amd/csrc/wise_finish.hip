@@ -37,6 +37,7 @@ namespace {
 constexpr int kLanes = 64;
 constexpr int kUnroll = 8;
 constexpr int kHeadsPerGroup = 16;  // waves (heads) per finish workgroup
+constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp32(uint32_t x) {
@@ -244,8 +245,11 @@ __device__ __forceinline__ UnitResult finish_unit(const FinishParams &p, const U
   const int D = p.head_dim;
   const bool stateful = p.support != nullptr && !ui.row_bad && ui.req != WISE_DENSE;
   const bool discover = stateful && (ui.eff == WISE_DISCOVER || ui.eff == WISE_DISCOVER_UNION);
+  // LSE route: no output; a row whose discovery window broke has nothing to do
+  const bool lse_mode = p.lse != nullptr;
+  if (lse_mode && !discover && !ui.row_bad) return UnitResult{false, 0};
 
-  // ---- loads: partials, tile stats, old support words ----
+  // ---- loads: partials, tile stats, old support words (and the LSE) ----
   constexpr int kDims = 2;  // head_dim <= 2 * 64
   const float *acc = p.part_acc + base * D;
   float v[kDims][kUnroll];
@@ -253,8 +257,9 @@ __device__ __forceinline__ UnitResult finish_unit(const FinishParams &p, const U
   for (int q = 0; q < kDims; ++q) {
     const int dd = lane + q * kLanes;
 #pragma unroll
-    for (int t = 0; t < kUnroll; ++t) v[q][t] = (dd < D && t < items) ? acc[t * D + dd] : 0.0f;
+    for (int t = 0; t < kUnroll; ++t) v[q][t] = (!lse_mode && dd < D && t < items) ? acc[t * D + dd] : 0.0f;
   }
+  const float lse = lse_mode ? p.lse[ui.u] : 0.0f;
   float2 ml_own[kMaxItemsPerUnit / kLanes];
 #pragma unroll
   for (int c = 0; c < kMaxItemsPerUnit / kLanes; ++c) {
@@ -282,38 +287,47 @@ __device__ __forceinline__ UnitResult finish_unit(const FinishParams &p, const U
     M = fmaxf(M, ml_own[c].x);
   }
   M = wave_max(M);
-  const bool err = items == 0 || __builtin_amdgcn_ballot_w64(bad_item) != 0ull;
-  float Lp = 0.0f;
+  bool err = items == 0 || __builtin_amdgcn_ballot_w64(bad_item) != 0ull;
+  float L = 1.0f;
+  if (lse_mode) {
+    // masses relative to the external kernel's normaliser: M = lse in base-2 units, L = 1
+    err = err || !__builtin_isfinite(lse);
+    M = lse * kLog2e;
+  } else {
+    float Lp = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kMaxItemsPerUnit / kLanes; ++c) {
-    const int i = c * kLanes + lane;
-    if (i < items) {
-      const float w = __builtin_amdgcn_exp2f(ml_own[c].x - M);
-      s_w[i] = w;
-      Lp = fmaf(ml_own[c].y, w, Lp);
+    for (int c = 0; c < kMaxItemsPerUnit / kLanes; ++c) {
+      const int i = c * kLanes + lane;
+      if (i < items) {
+        const float w = __builtin_amdgcn_exp2f(ml_own[c].x - M);
+        s_w[i] = w;
+        Lp = fmaf(ml_own[c].y, w, Lp);
+      }
     }
+    L = wave_sum(Lp);
   }
-  const float L = wave_sum(Lp);
   if (discover)
     for (int w = lane; w < kMaxWords; w += kLanes) s_bits[w] = 0u;
   wave_lds_sync();
+  if (!lse_mode) {
 #pragma unroll
-  for (int q = 0; q < kDims; ++q) {
-    const int dd = lane + q * kLanes;
-    if (dd >= D) break;
-    float a = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kUnroll; ++t)
-      if (t < items) a = fmaf(v[q][t], s_w[t], a);
-    for (int i0 = kUnroll; i0 < items; i0 += kUnroll) {
-      float x[kUnroll];
-#pragma unroll
-      for (int t = 0; t < kUnroll; ++t) x[t] = i0 + t < items ? acc[(i0 + t) * D + dd] : 0.0f;
+    for (int q = 0; q < kDims; ++q) {
+      const int dd = lane + q * kLanes;
+      if (dd >= D) break;
+      float a = 0.0f;
 #pragma unroll
       for (int t = 0; t < kUnroll; ++t)
-        if (i0 + t < items) a = fmaf(x[t], s_w[i0 + t], a);
+        if (t < items) a = fmaf(v[q][t], s_w[t], a);
+      for (int i0 = kUnroll; i0 < items; i0 += kUnroll) {
+        float x[kUnroll];
+#pragma unroll
+        for (int t = 0; t < kUnroll; ++t) x[t] = i0 + t < items ? acc[(i0 + t) * D + dd] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < kUnroll; ++t)
+          if (i0 + t < items) a = fmaf(x[t], s_w[i0 + t], a);
+      }
+      p.out[static_cast<int64_t>(ui.u) * D + dd] = err ? __builtin_nanf("") : a / L;
     }
-    p.out[static_cast<int64_t>(ui.u) * D + dd] = err ? __builtin_nanf("") : a / L;
   }
   if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
 

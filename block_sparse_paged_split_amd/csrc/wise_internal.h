@@ -73,8 +73,9 @@ struct FinishParams {
   const int32_t *ctx_len;
   float *out;
   const int32_t *row_code, *unit_items;
-  // per row, one atomic word: heads finished (bits 0..15), heads with an
-  // error (bits 16..31), blocks newly selected by the row's heads (32..63)
+  // per row, one atomic word for rows spanning several finish workgroups:
+  // workgroups finished (bits 0..15), heads with an error (bits 16..31),
+  // blocks newly selected by the row's heads (32..63)
   unsigned long long *row_done;
   const float2 *part_ml;
   const float *part_acc;
@@ -87,14 +88,19 @@ struct FinishParams {
   const int64_t *row_request, *row_position;
   float eta;
   unsigned long long *counters;
+  // [rows * heads] natural-log LSE of an external dense kernel, or NULL.
+  // When set, the finish selects from mass = l_b exp(m_b - lse) and writes
+  // no output (the preceding split read K only).
+  const float *lse;
 };
 
 // listed = plan kernel + persistent split over the compact item list (calls
 // with sparse rows); otherwise the static one-wave-per-item-slot grid.
+// k_only = read K only and keep tile stats (static grid, discovery modes).
 // cus = compute units of the current device (sizes the persistent grid);
 // ev_begin / ev_end (optional) are recorded right around the split kernel.
-hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, int cus, hipEvent_t ev_begin,
-                        hipEvent_t ev_end, hipStream_t stream);
+hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, int cus,
+                        hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_finish(const FinishParams &p, hipStream_t stream);
 
 }  // namespace wise

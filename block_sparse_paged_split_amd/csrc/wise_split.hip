@@ -201,9 +201,11 @@ __device__ __forceinline__ int support_scan(const SplitParams &p, int slot, int 
 // One work item: list entries [first, first + ntiles) of unit (r, h) --
 // either tiles first.. (all causal tiles) or the support's set bits of those
 // ranks, compacted into a per-wave list before the loop.  Writes the
-// item's partial (m, l, acc) and the tile stats.
+// item's partial (m, l, acc) and the tile stats.  kKOnly: K is read and the
+// scores' tile stats and (m, l) are kept, V and the accumulator are not
+// (discovery after an external dense kernel).
 // ---------------------------------------------------------------------------
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kKOnly>
 __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int h, int k, int n, bool sparse,
                                          int count, uint32_t word, int incl, int lane, int *tiles) {
   using G = Geo<kBf16, D>;
@@ -242,7 +244,7 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
   const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) +
                                                     (static_cast<int64_t>(u) * D + c * G::EPL) * G::E);
   const char *kh = static_cast<const char *>(p.k) + h * p.stride_head_b;  // wave-uniform
-  const char *vh = static_cast<const char *>(p.v) + h * p.stride_head_b;
+  const char *vh = kKOnly ? nullptr : static_cast<const char *>(p.v) + h * p.stride_head_b;
   const int32_t *bt = p.block_table + r * p.bt_stride;
   const int pmask = (1 << p.page_shift) - 1;
 
@@ -282,7 +284,7 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
       page = pbad ? 0 : page;
       const int64_t off = page * p.stride_page_b + ((t0 + j * G::TPI) & pmask) * p.stride_token_b;
       kr[j] = load16(kh + off + lane_off);
-      vr[j] = load16(vh + off + lane_off);
+      if constexpr (!kKOnly) vr[j] = load16(vh + off + lane_off);
     }
     // keep all 2*NI loads in flight together: no arithmetic moves above here
     __builtin_amdgcn_sched_barrier(0);
@@ -315,22 +317,26 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     const float beta = __builtin_amdgcn_exp2f(mb - m_new);
     l_run = l_run * alpha + lb * beta;
+    if constexpr (!kKOnly) {
 #pragma unroll
-    for (int e = 0; e < G::EPL; ++e) acc[e] *= alpha;
+      for (int e = 0; e < G::EPL; ++e) acc[e] *= alpha;
 #pragma unroll
-    for (int j = 0; j < G::NI; ++j) {
-      const bool valid = j * G::TPI + g < nv;
-      const u32x4 v = valid ? vr[j] : u32x4{0u, 0u, 0u, 0u};
-      axpy16<kBf16>(acc, pj[j] * beta, v);
+      for (int j = 0; j < G::NI; ++j) {
+        const bool valid = j * G::TPI + g < nv;
+        const u32x4 v = valid ? vr[j] : u32x4{0u, 0u, 0u, 0u};
+        axpy16<kBf16>(acc, pj[j] * beta, v);
+      }
     }
     m_run = m_new;
   }
 
   // ---- partial (m, l, acc) of this item, and the tile stats ----
-#pragma unroll
-  for (int e = 0; e < G::EPL; ++e) acc[e] = subgroup_sum<G::LPT>(acc[e]);
   const int64_t slot_idx = static_cast<int64_t>(u) * p.items_per_unit + k;
-  if (g == 0) {
+  if constexpr (!kKOnly) {
+#pragma unroll
+    for (int e = 0; e < G::EPL; ++e) acc[e] = subgroup_sum<G::LPT>(acc[e]);
+  }
+  if (!kKOnly && g == 0) {
     float4 *dst = reinterpret_cast<float4 *>(p.part_acc + slot_idx * D + c * G::EPL);
 #pragma unroll
     for (int e = 0; e < G::EPL; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
@@ -349,7 +355,7 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
 // Used when no row is sparse, so every unit's item count is known from its
 // context length and (nearly) every slot holds work.
 // ---------------------------------------------------------------------------
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kKOnly>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const SplitParams p) {
   __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
   const int lane = threadIdx.x & 63;
@@ -377,7 +383,10 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
   const bool sparse = !rp.bad && rp.eff == WISE_SPARSE;
   uint32_t word = 0u;
   int incl = 0;
-  const int count = sparse ? support_scan(p, rp.slot, h, nb, lane, word, incl) : nb;
+  // K-only calls have nothing to do for a row whose discovery window broke
+  const int count = (kKOnly && rp.eff == WISE_DENSE) ? 0
+                    : sparse                         ? support_scan(p, rp.slot, h, nb, lane, word, incl)
+                                                     : nb;
   const int items = (count + p.tiles_per_item - 1) / p.tiles_per_item;
   if (k == 0 && lane == 0) {
     p.unit_items[u] = items;
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
     }
   }
   if (k >= items) return;
-  run_item<kBf16, D>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave]);
+  run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave]);
 }
 
 // ---------------------------------------------------------------------------
@@ -474,7 +483,7 @@ void split_listed_kernel(const SplitParams p) {
     int incl = 0;
     const int nb = (n + kBlock - 1) / kBlock;
     const int count = sparse ? support_scan(p, slot, h, nb, lane, word, incl) : nb;
-    run_item<kBf16, D>(p, u, r, h, k, n, sparse, count, word, incl, lane, s_tiles[wave]);
+    run_item<kBf16, D, false>(p, u, r, h, k, n, sparse, count, word, incl, lane, s_tiles[wave]);
   }
 }
 
@@ -499,8 +508,8 @@ static int listed_groups_per_cu() {
 }
 
 template <bool kBf16, int D>
-static hipError_t launch_typed(const SplitParams &p, bool listed, int cus, hipEvent_t ev_begin, hipEvent_t ev_end,
-                               hipStream_t stream) {
+static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, int cus, hipEvent_t ev_begin,
+                               hipEvent_t ev_end, hipStream_t stream) {
   const dim3 block(64 * kWavesPerGroup);
   if (listed) {
     const int per_cu = listed_groups_per_cu<kBf16, D>();
@@ -514,7 +523,10 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, int cus, hipEv
   } else {
     const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
     if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((split_static_kernel<kBf16, D>), grid, block, 0, stream, p);
+    if (k_only)
+      hipLaunchKernelGGL((split_static_kernel<kBf16, D, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((split_static_kernel<kBf16, D, false>), grid, block, 0, stream, p);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -522,12 +534,17 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, int cus, hipEv
   return hipSuccess;
 }
 
-hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, int cus, hipEvent_t ev_begin,
-                        hipEvent_t ev_end, hipStream_t stream) {
-  if (dtype == WISE_BF16 && head_dim == 128) return launch_typed<true, 128>(p, listed, cus, ev_begin, ev_end, stream);
-  if (dtype == WISE_BF16 && head_dim == 64) return launch_typed<true, 64>(p, listed, cus, ev_begin, ev_end, stream);
-  if (dtype == WISE_F32 && head_dim == 128) return launch_typed<false, 128>(p, listed, cus, ev_begin, ev_end, stream);
-  if (dtype == WISE_F32 && head_dim == 64) return launch_typed<false, 64>(p, listed, cus, ev_begin, ev_end, stream);
+hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, int cus,
+                        hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
+  if (listed && k_only) return hipErrorInvalidValue;  // K-only calls have no sparse rows
+  if (dtype == WISE_BF16 && head_dim == 128)
+    return launch_typed<true, 128>(p, listed, k_only, cus, ev_begin, ev_end, stream);
+  if (dtype == WISE_BF16 && head_dim == 64)
+    return launch_typed<true, 64>(p, listed, k_only, cus, ev_begin, ev_end, stream);
+  if (dtype == WISE_F32 && head_dim == 128)
+    return launch_typed<false, 128>(p, listed, k_only, cus, ev_begin, ev_end, stream);
+  if (dtype == WISE_F32 && head_dim == 64)
+    return launch_typed<false, 64>(p, listed, k_only, cus, ev_begin, ev_end, stream);
   return hipErrorInvalidValue;
 }
 

@@ -141,6 +141,17 @@ def call(layer: DeviceLayer, ws: Workspace, mode: int, state: Optional[SupportSt
     W.wise_finish_select(a, s, ws.ptr, ws.nbytes, st)
 
 
+def call_lse(layer: DeviceLayer, ws: Workspace, lse, union: bool, state: SupportState,
+             layer_idx: int = 0, eta: float = 0.95, events=None,
+             stream: Optional[int] = None) -> None:
+    """One discovery depth by the LSE route: ``lse`` [R, H] fp32 on the device
+    is the external dense kernel's log-sum-exp."""
+    st = stream_handle() if stream is None else stream
+    a = layer.attn(events)
+    s = state.view(layer_idx, 1, eta)
+    W.wise_discover_lse(a, s, union, int(lse.data_ptr()), ws.ptr, ws.nbytes, st)
+
+
 class PreparedCall:
     """One (depth, layer) call with its ctypes arguments built once, so that
     issuing it costs two foreign calls (decode, finish)."""
@@ -186,6 +197,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
@@ -195,6 +207,10 @@ class HipEvents:
 
     def handle(self, i: int) -> int:
         return int(self.ev[i].value)
+
+    def record(self, i: int, stream: int) -> None:
+        if self.hip.hipEventRecord(self.ev[i], ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, i: int, j: int) -> float:
         ms = ctypes.c_float()

@@ -19,6 +19,7 @@ import argparse
 import csv
 import hashlib
 import json
+import re
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -69,7 +70,9 @@ def traffic(fetch_csv: str, write_csv: str, out_md: str, workload: str, mib: int
         raise SystemExit("calibration kernel not found in the counter output")
     scale_f = known / max(cal_f[0])
     scale_w = known / max(cal_w[0])
-    split = [k for k in f if "split_" in k and "kernel" in k]
+    # the decode split kernel (the K-only instantiation of the LSE route is not counted)
+    split = [k for k in f if "split_" in k and "kernel" in k
+             and not re.search(r"split_static_kernel<[^>]*, true>", k)]
     fk = [x for k in split for x in f[k]]
     wk = [x for k in split for x in w.get(k, [])]
     fetch_kib = sum(fk) / len(fk)

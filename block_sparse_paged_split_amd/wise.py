@@ -25,7 +25,7 @@ NUM_COUNTERS = 4
 BLOCK = 32
 
 EXPORTED = ("wise_workspace_size", "wise_decode_dense", "wise_decode_discover",
-            "wise_decode_sparse", "wise_finish_select", "wise_status_string")
+            "wise_decode_sparse", "wise_finish_select", "wise_discover_lse", "wise_status_string")
 
 
 class WiseTag(ctypes.Structure):
@@ -79,8 +79,9 @@ def lib() -> ctypes.CDLL:
         L.wise_decode_discover.argtypes = [P, S, ctypes.c_int32, V, ctypes.c_size_t, V]
         L.wise_decode_sparse.argtypes = [P, S, V, V, ctypes.c_size_t, V]
         L.wise_finish_select.argtypes = [P, S, V, ctypes.c_size_t, V]
+        L.wise_discover_lse.argtypes = [P, S, ctypes.c_int32, V, V, ctypes.c_size_t, V]
         for f in ("wise_decode_dense", "wise_decode_discover", "wise_decode_sparse",
-                  "wise_finish_select"):
+                  "wise_finish_select", "wise_discover_lse"):
             getattr(L, f).restype = ctypes.c_int
         L.wise_status_string.restype = ctypes.c_char_p
         L.wise_status_string.argtypes = [ctypes.c_int]
@@ -127,6 +128,12 @@ def wise_finish_select(a: WiseAttn, s: Optional[WiseSupport], ws: int, ws_bytes:
                        stream: int = 0) -> None:
     _check(lib().wise_finish_select(ctypes.byref(a), _ref(s), ws, ws_bytes, stream),
            "wise_finish_select")
+
+
+def wise_discover_lse(a: WiseAttn, s: WiseSupport, union_with_previous: bool, lse: int, ws: int,
+                      ws_bytes: int, stream: int = 0) -> None:
+    _check(lib().wise_discover_lse(ctypes.byref(a), ctypes.byref(s), int(bool(union_with_previous)),
+                                   lse, ws, ws_bytes, stream), "wise_discover_lse")
 
 
 # ----------------------------------------------------------------------------- torch marshalling

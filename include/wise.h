@@ -187,6 +187,29 @@ wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
 wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws,
                                size_t ws_bytes, void *stream);
 
+/*
+ * Discovery after an external dense decode (WISE pull request page, "What
+ * changes", second bullet: the FlashAttention route rereads K once to
+ * rebuild block mass from the kernel's LSE).  Every row DISCOVER
+ * (union_with_previous == 0) or DISCOVER_UNION (!= 0), with the tag rules
+ * of wise_decode_discover.  One call enqueues both kernels: a split-KV pass
+ * that reads q and K only and records every tile's (max, sum), then the
+ * selection, with block mass m_b -> l_b * exp(m_b - lse) instead of the
+ * merged (M, L); support, tags and counters are updated as by
+ * wise_finish_select.  No attention output is written: a->v_cache and
+ * a->out are not read and may be NULL; a->tile_stats is honoured.
+ *   lse  [rows, heads] fp32 device array: log(sum_t exp(scale * q.k_t))
+ *        over the row's ctx_len tokens, natural log (what FlashAttention's
+ *        decode reports as softmax LSE).  A non-finite entry is a data
+ *        error of its (row, head): counted in counters[WISE_CTR_ERRORS], the
+ *        row's discovery window is broken (tag discoveries = 0).
+ * Errors as for the other calls; lse == NULL or s == NULL is WISE_E_ARG.
+ * Uses the workspace like a decode + finish pair.
+ */
+wise_status wise_discover_lse(const wise_attn *a, const wise_support *s,
+                              int32_t union_with_previous, const float *lse, void *ws,
+                              size_t ws_bytes, void *stream);
+
 /* Static, human-readable name of a status. */
 const char *wise_status_string(wise_status st);
 

@@ -131,3 +131,94 @@ def check_call(w: synth.Workload, li: synth.LayerInputs, dev: harness.DeviceLaye
             assert rep.counters[W.CTR_SELECTED] == ref.counters[1]
             assert rep.counters[W.CTR_CAUSAL] == ref.counters[2]
     return rep
+
+
+# ----------------------------------------------------------------------------- LSE route
+
+def oracle_lse(w: synth.Workload, li: synth.LayerInputs, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """[R, H] fp32 log-sum-exp of every (row, head)'s scaled scores, from the
+    oracle: the stand-in for an external dense kernel's LSE.  Rows whose
+    context or pages are invalid (and rows not listed) get 0."""
+    R, H, d = li.q.shape
+    scale = O.default_scale(d)
+    out = np.zeros((R, H), np.float32)
+    for r in (range(R) if rows is None else rows):
+        n = int(li.ctx_len[r])
+        if not 1 <= n <= w.max_ctx:
+            continue
+        toks = np.arange(n)
+        pages = li.block_table[r][toks // w.page_size]
+        if np.any((pages < 0) | (pages >= li.num_pages)):
+            continue
+        qf = O.widen(li.q[r])
+        for h in range(H):
+            s = scale * (O.gather_tokens(li.k, li.block_table[r], toks, w.page_size, h) @ qf[h])
+            out[r, h] = O.row_lse(s)
+    return out
+
+
+def check_lse_call(w: synth.Workload, li: synth.LayerInputs, dev: harness.DeviceLayer,
+                   ws: harness.Workspace, state: harness.SupportState, lse: np.ndarray, *,
+                   union: bool, layer: int = 0, rows: Optional[Sequence[int]] = None,
+                   eta: Optional[float] = None) -> Report:
+    """One LSE-route discovery depth on the GPU against ``O.run_lse_call`` on
+    the same fp32 lse: supports (exact but for class A/B units), tile masses,
+    tags, counters, and ``out`` left untouched."""
+    import torch
+    R, H = li.q.shape[:2]
+    eta = w.eta if eta is None else eta
+    rows = list(range(R)) if rows is None else list(rows)
+    sup0 = state.support_numpy().copy()
+    tags0 = state.tags_numpy()
+    ctr0 = state.counters.cpu().numpy().copy()
+    dev.out.fill_(123.0)
+    lse_dev = torch.from_numpy(np.ascontiguousarray(lse, np.float32)).to(dev.q.device)
+    harness.call_lse(dev, ws, lse_dev, union, state, layer_idx=layer, eta=eta)
+    torch.cuda.synchronize()
+    assert bool((dev.out == 123.0).all()), "the LSE route wrote the attention output"
+    slot_of_row = None if state.slot_of_row is None else state.slot_of_row.cpu().numpy()
+    ref = O.run_lse_call(q=li.q, k_cache=li.k, block_table=li.block_table, ctx_len=li.ctx_len,
+                         page_size=w.page_size, num_pages=li.num_pages, max_ctx=w.max_ctx,
+                         lse=lse.astype(np.float64), union=union, support=sup0, tags=tags0,
+                         layer=layer, slot_of_row=slot_of_row,
+                         row_request=state.row_request.cpu().numpy(),
+                         row_position=state.row_position.cpu().numpy(), eta=eta, rows=rows)
+    rep = Report(units=len(rows) * H)
+    sup1 = state.support_numpy()
+    tags1 = state.tags_numpy()
+    rep.counters = state.counters.cpu().numpy() - ctr0
+    for r in rows:
+        if ref.effective[r] < 0:
+            continue
+        s = r if slot_of_row is None else int(slot_of_row[r])
+        for h in range(H):
+            unit = ref.units.get((r, h))
+            if unit is not None and unit.selection is not None:
+                a = unit.selection.near_eta(eta)
+                b = unit.selection.near_tie()
+                rep.near_eta += int(a)
+                rep.near_tie += int(b and not a)
+                if not np.array_equal(sup1[s, layer, h], ref.support[s, layer, h]):
+                    rep.support_mismatch += 1
+                    assert a or b, (f"LSE support of row {r} head {h} differs: gpu "
+                                    f"{O.bits_to_blocks(sup1[s, layer, h], 2048)} oracle "
+                                    f"{unit.selection.blocks} (K={unit.selection.K})")
+                if dev.tile_stats is not None:
+                    st = dev.tile_stats[r, h].cpu().numpy().astype(np.float64)
+                    nb = len(unit.mass)
+                    p_gpu = st[:nb, 1] * np.exp(st[:nb, 0] - float(lse[r, h]))
+                    err = np.abs(p_gpu - unit.mass)
+                    assert (err <= 1e-6 + 1e-5 * unit.mass).all(), \
+                        f"LSE block masses of row {r} head {h}: max {err.max():.3e}"
+            else:
+                assert np.array_equal(sup1[s, layer, h], sup0[s, layer, h]), \
+                    f"row {r} head {h} support touched"
+        for f in ("request", "position", "discoveries"):
+            assert tags1[s, layer][f] == ref.tags[s, layer][f], f"tag {f} of row {r}"
+    if len(rows) == R:
+        assert rep.counters[W.CTR_FALLBACKS] == ref.counters[0]
+        assert rep.counters[W.CTR_ERRORS] == ref.counters[3]
+        if rep.support_mismatch == 0:
+            assert rep.counters[W.CTR_SELECTED] == ref.counters[1]
+            assert rep.counters[W.CTR_CAUSAL] == ref.counters[2]
+    return rep

@@ -92,6 +92,8 @@ def call(lib, fn, a, s=None, ws=None, ws_bytes=None, extra=None):
         return lib.wise_decode_discover(pa, ps, 0, ws, wsb, None)
     if fn == "sparse":
         return lib.wise_decode_sparse(pa, ps, extra, ws, wsb, None)
+    if fn == "lse":
+        return lib.wise_discover_lse(pa, ps, 0, FAKE if extra is None else extra, ws, wsb, None)
     return lib.wise_finish_select(pa, ps, ws, wsb, None)
 
 
@@ -133,7 +135,7 @@ SUPPORT_CASES = [
 
 
 @pytest.mark.parametrize("name,kw,expect", SUPPORT_CASES, ids=[c[0] for c in SUPPORT_CASES])
-@pytest.mark.parametrize("fn", ["discover", "sparse"])
+@pytest.mark.parametrize("fn", ["discover", "sparse", "lse"])
 def test_support_validation(lib, name, kw, expect, fn):
     s = None if kw is None else good_support(**kw)
     assert call(lib, fn, good_attn(), s) == expect
@@ -144,3 +146,18 @@ def test_workspace_validation(lib):
     # too small (a fake, aligned address is never touched: the size check fails first)
     assert call(lib, "dense", good_attn(), ws=1 << 20, ws_bytes=need - 1) == W.WISE_E_WORKSPACE
     assert call(lib, "finish", good_attn(), ws=(1 << 20) + 64, ws_bytes=need) == W.WISE_E_WORKSPACE
+
+
+def test_lse_route_validation(lib):
+    """wise_discover_lse: the LSE array is required and 4-byte aligned, V and
+    out are optional (only the workspace check is left to fail), K is not."""
+    a, s = good_attn(), good_support()
+    assert call(lib, "lse", a, s, extra=None) == W.WISE_E_WORKSPACE      # FAKE lse, no workspace
+    assert lib.wise_discover_lse(ctypes.byref(a), ctypes.byref(s), 0, None, 0, 0, None) == W.WISE_E_ARG
+    assert call(lib, "lse", a, s, extra=FAKE + 2) == W.WISE_E_ARG
+    assert call(lib, "lse", good_attn(v_cache=None, out=None), s) == W.WISE_E_WORKSPACE
+    assert call(lib, "lse", good_attn(k_cache=None), s) == W.WISE_E_ARG
+    assert call(lib, "lse", a, None) == W.WISE_E_ARG
+    # the other entry points still need V and out
+    assert call(lib, "dense", good_attn(v_cache=None)) == W.WISE_E_ARG
+    assert call(lib, "finish", good_attn(out=None)) == W.WISE_E_ARG
