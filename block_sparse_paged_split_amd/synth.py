@@ -92,6 +92,7 @@ class Workload:
     schedule: Tuple[int, ...] = (DISCOVER, DISCOVER_UNION, SPARSE, SPARSE)
     eta: float = 0.95
     spare_pages: int = 3
+    shared_hot: bool = False        # one set of planted blocks per (row, layer), shared by the heads
     note: str = ""
 
     @property
@@ -143,6 +144,12 @@ WORKLOADS: Dict[str, Workload] = {
         name="match8k", rows=64, heads=16, head_dim=128, dtype="bf16", page_size=16,
         shuffle=True, alpha=8.0, seed=13, ctx=8192, hot=38,
         note="supplementary: ~0.15 union density at 8K"),
+    # supplementary, for the head-union page-granular route: the heads of a row
+    # share their planted blocks (heads attending the same positions)
+    "shared8k": Workload(
+        name="shared8k", rows=64, heads=16, head_dim=128, dtype="bf16", page_size=16,
+        shuffle=True, alpha=8.0, seed=14, ctx=8192, hot=38, shared_hot=True,
+        note="supplementary: match8k with planted blocks shared by a row's heads"),
 }
 
 
@@ -188,11 +195,11 @@ def hot_blocks(w: Workload, layer: int, row: int, nb: int) -> np.ndarray:
     """
     g = _rng(w.seed, _S_HOT, layer, row)
     out = []
-    for _ in range(w.heads):
+    for _ in range(1 if w.shared_hot else w.heads):
         k = w.hot if w.hot is not None else int(g.integers(w.hot_range[0], w.hot_range[1] + 1))
         k = min(k, nb)
         out.append(np.sort(g.choice(nb, size=k, replace=False)).astype(np.int64))
-    return out
+    return out * w.heads if w.shared_hot else out
 
 
 def row_qkv(w: Workload, depth: int, layer: int, row: int, n: int):

@@ -36,7 +36,10 @@ Where the page is silent, this oracle takes these readings:
     kernel's LSE, rereading K) takes lse = log sum_t exp(s_t) in natural-log
     units over the row's whole context; a block's mass is then the sum of
     exp(s_t - lse) over its tokens, selection as above; a non-finite lse is a
-    data error of its unit.
+    data error of its unit;
+  * the page's head-union support at page granularity keeps a KV page when
+    it holds a valid token of any block selected for any head of the row's
+    (slot, layer); every head then attends all tokens of the kept pages.
 
 Every function here has a pin in ``tests/test_oracle_pins.py``.
 """
@@ -458,6 +461,114 @@ def run_lse_call(*, q, k_cache, block_table, ctx_len, page_size: int, num_pages:
         tg[slot, layer] = update_tag(tg[slot, layer], req, eff, int(row_request[r]),
                                      int(row_position[r]), row_err)
     return CallResult(None, sup, tg, counters, eff_all, units)
+
+
+# ----------------------------------------------------------------------------
+# O10 head-union, page-granular support through a compacted page table: the
+#     page's FlashAttention route ("What changes", second bullet) lets a sparse
+#     row attend the union over its heads of the layer's support, widened to
+#     whole KV pages and handed to the attention kernel as a shorter page table.
+# ----------------------------------------------------------------------------
+
+def head_union_blocks(words: np.ndarray, nb: int) -> np.ndarray:
+    """Blocks set for any head: words is [heads, W] of one (slot, layer)."""
+    u = set()
+    for h in range(words.shape[0]):
+        u.update(int(b) for b in bits_to_blocks(words[h], nb))
+    return np.array(sorted(u), dtype=np.int64)
+
+
+def union_pages(blocks: Sequence[int], n: int, page_size: int) -> np.ndarray:
+    """Logical pages j < ceil(n/P) holding a token of a selected block."""
+    pages = set()
+    for b in blocks:
+        lo, hi = b * BLOCK, min(n, b * BLOCK + BLOCK) - 1      # the block's valid tokens
+        pages.update(range(lo // page_size, hi // page_size + 1))
+    return np.array(sorted(pages), dtype=np.int64)
+
+
+def page_tokens(pages: Sequence[int], n: int, page_size: int) -> np.ndarray:
+    """Logical token positions of the given pages, in order (clipped to n)."""
+    return np.array([t for j in pages for t in range(j * page_size, min(n, j * page_size + page_size))],
+                    dtype=np.int64)
+
+
+@dataclasses.dataclass
+class PageUnionResult:
+    out: np.ndarray                          # [R, H, d] fp64, NaN for error rows
+    tables: Dict                             # r -> compacted physical page list
+    ctx: np.ndarray                          # [R] compacted context length
+    counters: np.ndarray                     # fallback, -, -, errors (per (row, head))
+    pages: Dict                              # r -> kept logical pages
+
+
+def run_page_union_call(*, q, k_cache, v_cache, block_table, ctx_len, page_size: int,
+                        num_pages: int, max_ctx: int, support: np.ndarray, tags: np.ndarray,
+                        scale: float = 0.0, layer: int = 0,
+                        slot_of_row: Optional[Sequence[int]] = None,
+                        row_request: Optional[Sequence[int]] = None,
+                        row_position: Optional[Sequence[int]] = None, required: int = 1,
+                        row_modes: Optional[Sequence[int]] = None,
+                        rows: Optional[Sequence[int]] = None) -> PageUnionResult:
+    """One reuse depth by the head-union page route.  Row modes: SPARSE
+    (default) attends the pages holding any block of the union over its heads
+    of the (slot, layer) support, when the tag admits reuse (as ``plan_row``);
+    otherwise, and for DENSE rows, every causal page.  The compacted table
+    lists the kept pages' physical ids in logical order and the compacted
+    context is the number of tokens they hold, so every kept page but the
+    last is full.  Every head of a row attends the same tokens, renormalised
+    within them.  Data errors (context outside [1, max_ctx], another mode, a
+    slot out of range, an empty union, a kept page id out of range) give NaN
+    for every head of the row and count one error per head.
+    """
+    R, H, d = q.shape
+    P = page_size
+    scale = scale if scale else default_scale(d)
+    out = np.full((R, H, d), np.nan)
+    ctx_out = np.zeros(R, dtype=np.int64)
+    tables, kept = {}, {}
+    counters = np.zeros(4, dtype=np.int64)
+    slots = support.shape[0]
+    for r in (range(R) if rows is None else rows):
+        n = int(ctx_len[r])
+        req = SPARSE if row_modes is None else int(row_modes[r])
+        if req not in (DENSE, SPARSE):
+            counters[3] += H
+            continue
+        if not 1 <= n <= max_ctx:
+            ctx_out[r] = n
+            counters[3] += H
+            continue
+        npg = (n + P - 1) // P
+        pages = np.arange(npg)
+        if req == SPARSE:
+            slot = r if slot_of_row is None else int(slot_of_row[r])
+            if not 0 <= slot < slots:
+                counters[3] += H
+                continue
+            eff, fb = plan_row(SPARSE, tags[slot, layer], int(row_request[r]), int(row_position[r]),
+                               required)
+            counters[0] += int(fb)
+            if eff == SPARSE:
+                blocks = head_union_blocks(support[slot, layer], num_blocks(n))
+                if len(blocks) == 0:
+                    counters[3] += H
+                    continue
+                pages = union_pages(blocks, n, P)
+        phys = np.asarray(block_table[r])[pages]
+        kept[r] = pages
+        tables[r] = phys
+        ctx_out[r] = len(page_tokens(pages, n, P))
+        if np.any((phys < 0) | (phys >= num_pages)):
+            counters[3] += H
+            continue
+        toks = page_tokens(pages, n, P)
+        qf = widen(q[r])
+        for h in range(H):
+            Kf = gather_tokens(k_cache, block_table[r], toks, P, h)
+            Vf = gather_tokens(v_cache, block_table[r], toks, P, h)
+            out[r, h] = dense_attention(qf[h], Kf, Vf, scale)["o"]
+    return PageUnionResult(out, tables, ctx_out, counters, kept)
 
 
 def density(counters: Sequence[int]) -> float:

@@ -471,6 +471,91 @@ def test_lse_call_matches_tile_route_and_unions():
     assert np.array_equal(e.support[0, 0, 0], ref.support[0, 0, 0])
 
 
+# ----------------------------------------------------------------------------- O10 head-union page route
+
+@pytest.mark.parametrize("P", [8, 16, 32, 64, 256])
+def test_union_pages_brute_force(P):
+    """Kept pages are exactly the pages holding a valid token of a selected
+    block (token-by-token enumeration), and the compacted token sequence is
+    the kept tokens in order, every kept page but the last full."""
+    rng = np.random.default_rng(P)
+    for n in (1, 31, 33, 100, 257, 1000):
+        nb = (n + 31) // 32
+        for _ in range(5):
+            blocks = np.sort(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False))
+            brute = sorted({t // P for t in range(n) if (t // 32) in set(blocks.tolist())})
+            got = O.union_pages(blocks, n, P)
+            assert got.tolist() == brute
+            toks = O.page_tokens(got, n, P)
+            assert toks.tolist() == [t for t in range(n) if t // P in set(brute)]
+            # compacted position i is token kept_pages[i // P] * P + i % P
+            i = np.arange(len(toks))
+            assert np.array_equal(got[i // P] * P + i % P, toks)
+
+
+def test_head_union_blocks():
+    words = np.array([[0b1001, 0], [0b0110, 1 << 3], [0, 0]], dtype=np.uint32)
+    assert O.head_union_blocks(words, 40).tolist() == [0, 1, 2, 3, 35]
+    assert O.head_union_blocks(words, 35).tolist() == [0, 1, 2, 3]     # bits past nb ignored
+    assert O.head_union_blocks(np.zeros((2, 1), np.uint32), 5).tolist() == []
+
+
+def test_page_union_call():
+    """All blocks set: the compacted table is the row's table and the output
+    is dense attention.  A sparse union: every head attends exactly the kept
+    pages' tokens (brute-force softmax).  A stale tag falls back to every
+    page.  A large page turns one selected block into its whole page."""
+    rng = np.random.default_rng(41)
+    case, Kl, Vl = paged_case(rng, 150, H=2, P=16)
+    sup, tags = state(heads=2)
+    tags[0, 0] = (7, 42, 2, 0)
+    common = dict(layer=0, row_request=[7], row_position=[42], required=2)
+    d = O.run_call(**case, modes=[O.DENSE])
+    full = sup.copy()
+    full[...] = 0x1F
+    res = O.run_page_union_call(**case, support=full, tags=tags, **common)
+    assert res.tables[0].tolist() == case["block_table"][0, :10].tolist() and res.ctx[0] == 150
+    np.testing.assert_allclose(res.out, d.out, atol=1e-14)
+    # head 0 selects block 1, head 1 selects block 4 (tokens 128..149)
+    part = sup.copy()
+    part[0, 0, 0, 0] = 1 << 1
+    part[0, 0, 1, 0] = 1 << 4
+    res = O.run_page_union_call(**case, support=part, tags=tags, **common)
+    assert res.pages[0].tolist() == [2, 3, 8, 9] and res.ctx[0] == 16 * 3 + 6
+    assert res.tables[0].tolist() == case["block_table"][0, [2, 3, 8, 9]].tolist()
+    toks = list(range(32, 64)) + list(range(128, 150))
+    for h in range(2):
+        ref, _ = brute_softmax_attention(case["q"][0, h].astype(float).tolist(),
+                                         Kl[h][toks].astype(float).tolist(),
+                                         Vl[h][toks].astype(float).tolist(), 1 / math.sqrt(8))
+        np.testing.assert_allclose(res.out[0, h], ref, atol=1e-12)
+    assert res.counters.tolist() == [0, 0, 0, 0]
+    # stale position: dense fallback over every page
+    stale = O.run_page_union_call(**case, support=part, tags=tags,
+                                  **dict(common, row_position=[43]))
+    assert stale.counters[0] == 1 and stale.ctx[0] == 150
+    np.testing.assert_allclose(stale.out, d.out, atol=1e-14)
+    # empty union: a data error for every head
+    empty = O.run_page_union_call(**case, support=sup, tags=tags, **common)
+    assert empty.counters[3] == 2 and np.isnan(empty.out).all() and empty.ctx[0] == 0
+    # a bad id in a kept page poisons every head of the row; in a dropped page it does nothing
+    bad = dict(case)
+    bad["block_table"] = case["block_table"].copy()
+    bad["block_table"][0, 5] = case["num_pages"] + 3
+    ok = O.run_page_union_call(**bad, support=part, tags=tags, **common)
+    assert ok.counters[3] == 0 and not np.isnan(ok.out).any()
+    bad["block_table"][0, 8] = -2
+    hit = O.run_page_union_call(**bad, support=part, tags=tags, **common)
+    assert hit.counters[3] == 2 and np.isnan(hit.out).all()
+    # one selected block inside a 256-token page keeps the whole page
+    case2, _, _ = paged_case(rng, 600, H=1, P=256)
+    one = np.zeros((1, 1, 1, 1), np.uint32)
+    one[0, 0, 0, 0] = 1 << 9                                 # tokens 288..319, page 1
+    r2 = O.run_page_union_call(**case2, support=one, tags=tags[:, :1], layer=0,
+                               row_request=[7], row_position=[42], required=2)
+    assert r2.pages[0].tolist() == [1] and r2.ctx[0] == 256
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def test_pins_catch_planted_mistakes(monkeypatch):
@@ -505,7 +590,14 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     def lse_full_blocks(s, lse):                # the partial last block dropped
         return real_lse_mass(s[: 32 * (len(s) // 32)] if len(s) >= 32 else s, lse)
 
+    real_union_pages = O.union_pages
+
+    def pages_whole_block(blocks, n, P):        # the block's end not clipped to the context
+        return np.array(sorted({j for b in blocks for j in range(32 * b // P, (32 * b + 31) // P + 1)}),
+                        dtype=np.int64)
+
     planted = [
+        ("union_pages", pages_whole_block, lambda: test_union_pages_brute_force(8)),
         ("eta_select", strict_cut, lambda: test_selection_dominant_and_single_block()),
         ("eta_select", index_desc, lambda: test_selection_tie_break_equal_masses()),
         ("block_mass", no_norm, lambda: test_tile_stats_and_mass(95)),
@@ -514,7 +606,7 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         ("lse_block_mass", lse_full_blocks, lambda: test_lse_block_mass_closed_form()),
     ]
     reals = {"eta_select": real_select, "block_mass": real_mass, "tile_stats": real_stats,
-             "lse_block_mass": real_lse_mass}
+             "lse_block_mass": real_lse_mass, "union_pages": real_union_pages}
     for name, fn, pin in planted:
         monkeypatch.setattr(O, name, fn)
         with pytest.raises(AssertionError):
