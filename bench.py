@@ -15,6 +15,7 @@ row is one query row attended at one (depth, layer).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import dataclasses
 import json
 import os
@@ -233,6 +234,8 @@ def main():
     ap.add_argument("--no-dense-reference", action="store_true")
     ap.add_argument("--no-lse-route", action="store_true",
                     help="skip the timing of discovery by the LSE route")
+    ap.add_argument("--no-page-route", action="store_true",
+                    help="skip the timing of the head-union page route")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (for counter-collection runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -400,6 +403,62 @@ def main():
                                      "GBps": round(lbytes / (sms * 1e-3) / 1e9, 1),
                                      "note": "K-only split + LSE selection, eager back-to-back calls; "
                                              "not part of a step"}
+
+    # ---- reuse depths by the head-union page route: compaction + dense decode over it ----
+    if not args.no_page_route and not plan.mixed:
+        sparse_keys = [key for _, key in plan.calls[0] if key[0] == "sparse"]
+        if sparse_keys:
+            plan.setup(0, sh)
+            step(0, sh)                      # replica 0's discovery supports, untimed
+            torch.cuda.synchronize()
+            pus = [(harness.PageUnion(plan.kv[(0, depth, layer % plan.kv_layers)]), layer)
+                   for _, depth, layer in sparse_keys]
+            for pu, layer in pus:
+                pu.compact(plan.state, layer, w.discoveries, stream=sh)
+                pu.attend(plan.ws, None, layer, stream=sh)
+            n_it = max(20, 2 * len(pus))
+            ev4 = harness.HipEvents(4 * n_it + 2)
+            L = W.lib()
+            prepared = []                    # ctypes arguments built once: issuing stays ahead of the GPU
+            for pu, layer in pus:
+                a_c, s_c, a_d = pu.layer.attn(), plan.state.view(layer, w.discoveries, w.eta), pu.attend_attn()
+                prepared.append((a_c, s_c, a_d, int(pu.bt.data_ptr()), pu.bt.stride(0), int(pu.ctx.data_ptr())))
+            ev4.record(4 * n_it, sh)
+            for it in range(n_it):           # back to back
+                a_c, s_c, a_d, bt_p, bt_s, ctx_p = prepared[it % len(prepared)]
+                ev4.record(4 * it, sh)
+                st = L.wise_compact_pages(ctypes.byref(a_c), ctypes.byref(s_c), None, bt_p, bt_s, ctx_p, sh)
+                ev4.record(4 * it + 1, sh)
+                a_d.ev_split_begin, a_d.ev_split_end = ev4.handle(4 * it + 2), ev4.handle(4 * it + 3)
+                st |= L.wise_decode_dense(ctypes.byref(a_d), plan.ws.ptr, plan.ws.nbytes, sh)
+                st |= L.wise_finish_select(ctypes.byref(a_d), None, plan.ws.ptr, plan.ws.nbytes, sh)
+                if st != W.WISE_OK:
+                    raise W.WiseError(st, "page route")
+            ev4.record(4 * n_it + 1, sh)
+            torch.cuda.synchronize()
+            comp_ms = np.array([ev4.elapsed_ms(4 * it, 4 * it + 1) for it in range(n_it)])
+            split_ms = np.array([ev4.elapsed_ms(4 * it + 2, 4 * it + 3) for it in range(n_it)])
+            e = 2 if w.dtype == "bf16" else 4
+            P, H, d = w.page_size, w.heads, w.head_dim
+            by, kept_pages, all_pages = [], 0, 0
+            for pu, _ in pus:
+                c = pu.ctx.cpu().numpy().astype(np.int64)
+                by.append(int((H * (2 * c * d * e + d * e) + 4 * ((c + P - 1) // P)).sum()))
+                kept_pages += int(((c + P - 1) // P).sum())
+                all_pages += int(((plan.ctx.astype(np.int64) + P - 1) // P).sum())
+            sbytes = float(np.mean([by[it % len(pus)] for it in range(n_it)]))
+            total_us = float(comp_ms.mean() + split_ms.mean()) * 1e3
+            entry = {"compact_us": round(float(comp_ms.mean()) * 1e3, 2),
+                     "split_us": round(float(split_ms.mean()) * 1e3, 2),
+                     "call_us": round(ev4.elapsed_ms(4 * n_it, 4 * n_it + 1) / n_it * 1e3, 2),
+                     "page_density": round(kept_pages / max(1, all_pages), 4),
+                     "algorithmic_MB": round(sbytes / 1e6, 3),
+                     "GBps": round(sbytes / (float(split_ms.mean()) * 1e-3) / 1e9, 1),
+                     "note": "head-union pages of the reuse depths; compaction + dense decode over "
+                             "the compacted table, eager back-to-back"}
+            if "dense_same_kv" in modes_out:
+                entry["speedup_vs_dense"] = round(modes_out["dense_same_kv"]["split_us"] / total_us, 3)
+            modes_out["page_union"] = entry
 
     rows_per_step = w.rows * calls
     out = {

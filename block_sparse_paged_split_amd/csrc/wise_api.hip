@@ -298,6 +298,44 @@ wise_status wise_discover_lse(const wise_attn *a, const wise_support *s, int32_t
   return finish(a, s, lse, ws, ws_bytes, stream);
 }
 
+wise_status wise_compact_pages(const wise_attn *a, const wise_support *s, const uint8_t *row_mode,
+                               int32_t *bt_out, int32_t bt_out_stride, int32_t *ctx_out, void *stream) {
+  Layout L;
+  wise_status st = check_attn(a, &L, true);
+  if (st != WISE_OK) return st;
+  st = check_support(a, s, L);
+  if (st != WISE_OK) return st;
+  if (!bt_out || !ctx_out || !aligned(bt_out, 4) || !aligned(ctx_out, 4)) return WISE_E_ARG;
+  if (bt_out == a->block_table || ctx_out == a->ctx_len) return WISE_E_ARG;  // not in place
+  const int64_t need = (static_cast<int64_t>(a->max_ctx) + a->page_size - 1) / a->page_size;
+  if (bt_out_stride < need) return WISE_E_ARG;
+  PageParams p{};
+  p.rows = a->rows;
+  p.heads = a->heads;
+  p.max_ctx = a->max_ctx;
+  p.page_shift = log2i(a->page_size);
+  p.block_table = a->block_table;
+  p.bt_stride = a->bt_stride;
+  p.ctx_len = a->ctx_len;
+  p.row_mode = row_mode;
+  p.support = s->support;
+  p.slots = s->slots;
+  p.layers = s->layers;
+  p.layer = s->layer;
+  p.words = s->words;
+  p.required = s->discoveries_required;
+  p.slot_of_row = s->slot_of_row;
+  p.tags = s->tags;
+  p.row_request = s->row_request;
+  p.row_position = s->row_position;
+  p.counters = reinterpret_cast<unsigned long long *>(s->counters);
+  p.bt_out = bt_out;
+  p.bt_out_stride = bt_out_stride;
+  p.ctx_out = ctx_out;
+  if (launch_compact_pages(p, static_cast<hipStream_t>(stream)) != hipSuccess) return WISE_E_HIP;
+  return WISE_OK;
+}
+
 const char *wise_status_string(wise_status st) {
   switch (st) {
     case WISE_OK: return "ok";

@@ -94,6 +94,24 @@ struct FinishParams {
   const float *lse;
 };
 
+// Head-union page compaction of one reuse depth (see wise_pages.hip).
+struct PageParams {
+  int32_t rows, heads, max_ctx, page_shift;
+  const int32_t *block_table;
+  int32_t bt_stride;
+  const int32_t *ctx_len;
+  const uint8_t *row_mode;  // NULL = every row SPARSE
+  const uint32_t *support;
+  int32_t slots, layers, layer, words, required;
+  const int32_t *slot_of_row;
+  const wise_tag *tags;
+  const int64_t *row_request, *row_position;
+  unsigned long long *counters;
+  int32_t *bt_out;
+  int32_t bt_out_stride;
+  int32_t *ctx_out;
+};
+
 // listed = plan kernel + persistent split over the compact item list (calls
 // with sparse rows); otherwise the static one-wave-per-item-slot grid.
 // k_only = read K only and keep tile stats (static grid, discovery modes).
@@ -102,5 +120,6 @@ struct FinishParams {
 hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, int cus,
                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_finish(const FinishParams &p, hipStream_t stream);
+hipError_t launch_compact_pages(const PageParams &p, hipStream_t stream);
 
 }  // namespace wise

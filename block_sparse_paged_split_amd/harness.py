@@ -152,6 +152,43 @@ def call_lse(layer: DeviceLayer, ws: Workspace, lse, union: bool, state: Support
     W.wise_discover_lse(a, s, union, int(lse.data_ptr()), ws.ptr, ws.nbytes, st)
 
 
+class PageUnion:
+    """Compacted page table and context of one reuse depth by the head-union
+    page route, and the dense attention call over them."""
+
+    def __init__(self, layer: DeviceLayer, device="cuda"):
+        torch = _torch()
+        R = layer.q.shape[0]
+        width = layer.block_table.shape[1]
+        self.bt = torch.full((R, width), -1, dtype=torch.int32, device=device)
+        self.ctx = torch.zeros(R, dtype=torch.int32, device=device)
+        self.layer = layer
+
+    def compact(self, state: SupportState, layer_idx: int = 0, required: int = 2, row_mode=None,
+                stream: Optional[int] = None) -> None:
+        st = stream_handle() if stream is None else stream
+        a = self.layer.attn()
+        s = state.view(layer_idx, required, 0.95)
+        W.wise_compact_pages(a, s, None if row_mode is None else int(row_mode.data_ptr()),
+                             int(self.bt.data_ptr()), self.bt.stride(0), int(self.ctx.data_ptr()), st)
+
+    def attend_attn(self, events=None) -> W.WiseAttn:
+        """The attention call's operands: the layer's, over the compacted table."""
+        a = self.layer.attn(events)
+        a.block_table = int(self.bt.data_ptr())
+        a.bt_stride = self.bt.stride(0)
+        a.ctx_len = int(self.ctx.data_ptr())
+        return a
+
+    def attend(self, ws: "Workspace", state: Optional[SupportState] = None, layer_idx: int = 0,
+               events=None, stream: Optional[int] = None) -> None:
+        st = stream_handle() if stream is None else stream
+        a = self.attend_attn(events)
+        s = state.view(layer_idx, 1, 0.95) if state is not None else None
+        W.wise_decode_dense(a, ws.ptr, ws.nbytes, st)
+        W.wise_finish_select(a, s, ws.ptr, ws.nbytes, st)
+
+
 class PreparedCall:
     """One (depth, layer) call with its ctypes arguments built once, so that
     issuing it costs two foreign calls (decode, finish)."""

@@ -25,7 +25,8 @@ NUM_COUNTERS = 4
 BLOCK = 32
 
 EXPORTED = ("wise_workspace_size", "wise_decode_dense", "wise_decode_discover",
-            "wise_decode_sparse", "wise_finish_select", "wise_discover_lse", "wise_status_string")
+            "wise_decode_sparse", "wise_finish_select", "wise_discover_lse", "wise_compact_pages",
+            "wise_status_string")
 
 
 class WiseTag(ctypes.Structure):
@@ -80,8 +81,9 @@ def lib() -> ctypes.CDLL:
         L.wise_decode_sparse.argtypes = [P, S, V, V, ctypes.c_size_t, V]
         L.wise_finish_select.argtypes = [P, S, V, ctypes.c_size_t, V]
         L.wise_discover_lse.argtypes = [P, S, ctypes.c_int32, V, V, ctypes.c_size_t, V]
+        L.wise_compact_pages.argtypes = [P, S, V, V, ctypes.c_int32, V, V]
         for f in ("wise_decode_dense", "wise_decode_discover", "wise_decode_sparse",
-                  "wise_finish_select", "wise_discover_lse"):
+                  "wise_finish_select", "wise_discover_lse", "wise_compact_pages"):
             getattr(L, f).restype = ctypes.c_int
         L.wise_status_string.restype = ctypes.c_char_p
         L.wise_status_string.argtypes = [ctypes.c_int]
@@ -134,6 +136,12 @@ def wise_discover_lse(a: WiseAttn, s: WiseSupport, union_with_previous: bool, ls
                       ws_bytes: int, stream: int = 0) -> None:
     _check(lib().wise_discover_lse(ctypes.byref(a), ctypes.byref(s), int(bool(union_with_previous)),
                                    lse, ws, ws_bytes, stream), "wise_discover_lse")
+
+
+def wise_compact_pages(a: WiseAttn, s: WiseSupport, row_mode: Optional[int], bt_out: int,
+                       bt_out_stride: int, ctx_out: int, stream: int = 0) -> None:
+    _check(lib().wise_compact_pages(ctypes.byref(a), ctypes.byref(s), row_mode, bt_out, bt_out_stride,
+                                    ctx_out, stream), "wise_compact_pages")
 
 
 # ----------------------------------------------------------------------------- torch marshalling

@@ -183,7 +183,8 @@ wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
 /* Merge the splits of the preceding decode call into a->out; for discovery
  * rows run the eta selection, write/OR the support, update the tags and
  * the counters.  `a` and `s` must describe the same call as the decode
- * call (s == NULL after wise_decode_dense). */
+ * call.  After wise_decode_dense, s may be NULL; if given, only its
+ * counters are touched (data errors), never the support or the tags. */
 wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws,
                                size_t ws_bytes, void *stream);
 
@@ -209,6 +210,39 @@ wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *
 wise_status wise_discover_lse(const wise_attn *a, const wise_support *s,
                               int32_t union_with_previous, const float *lse, void *ws,
                               size_t ws_bytes, void *stream);
+
+/*
+ * Head-union, page-granular support through a compacted page table (WISE
+ * pull request page, "What changes", second bullet: on the FlashAttention
+ * route a sparse row attends the per-layer head union of its support at
+ * page granularity through a compacted page table).  For every row:
+ *   SPARSE (row_mode == NULL, or row_mode[r] == WISE_SPARSE) whose tag admits
+ *     reuse (as wise_decode_sparse): page j of the row is kept when one of
+ *     its valid tokens lies in a block set for ANY head of the (slot, layer)
+ *     support; bt_out[r] lists the kept pages' physical ids in logical order
+ *     and ctx_out[r] the tokens they hold ((kept - 1) * page_size + the
+ *     valid tokens of the last kept page);
+ *   SPARSE whose tag does not admit reuse: every page (a dense fallback,
+ *     counted in counters[WISE_CTR_FALLBACKS]);
+ *   DENSE: every page.
+ * Every head of a row then attends the same tokens: run any paged dense
+ * decode over (bt_out, ctx_out), e.g. wise_decode_dense with a copy of `a`
+ * whose block_table, bt_stride and ctx_len are bt_out, bt_out_stride and
+ * ctx_out, followed by wise_finish_select(copy, s) (a dense call touches no
+ * support state; given s, its finish counts data errors).
+ *   bt_out   [rows, bt_out_stride] int32 device array, bt_out_stride >=
+ *            ceil(max_ctx / page_size); entries past a row's compacted
+ *            pages are left untouched.  Must not be a->block_table.
+ *   ctx_out  [rows] int32 device array; must not be a->ctx_len.
+ * Data errors are left for the attention call to flag: a context outside
+ * [1, max_ctx] is copied as is; another row mode, a slot out of range or an
+ * empty head union give ctx_out = 0.  `a` describes the attention call (q,
+ * k_cache, block_table, ctx_len, sizes); v_cache and out are not read.
+ * Enqueues one kernel; no workspace.
+ */
+wise_status wise_compact_pages(const wise_attn *a, const wise_support *s,
+                               const uint8_t *row_mode, int32_t *bt_out,
+                               int32_t bt_out_stride, int32_t *ctx_out, void *stream);
 
 /* Static, human-readable name of a status. */
 const char *wise_status_string(wise_status st);

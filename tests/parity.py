@@ -32,6 +32,7 @@ class Report:
     near_tie: int = 0          # class B
     support_mismatch: int = 0  # mismatching units (must be <= near_eta + near_tie)
     counters: Optional[np.ndarray] = None
+    page_density: float = 0.0  # head-union page route: kept pages / causal pages
 
 
 def assert_close(got, ref, dtype, what, report: Report):
@@ -221,4 +222,58 @@ def check_lse_call(w: synth.Workload, li: synth.LayerInputs, dev: harness.Device
         if rep.support_mismatch == 0:
             assert rep.counters[W.CTR_SELECTED] == ref.counters[1]
             assert rep.counters[W.CTR_CAUSAL] == ref.counters[2]
+    return rep
+
+
+# ----------------------------------------------------------------------------- head-union page route
+
+def check_page_union(w: synth.Workload, li: synth.LayerInputs, dev: harness.DeviceLayer,
+                     ws: harness.Workspace, state: harness.SupportState, *, layer: int = 0,
+                     required: Optional[int] = None, row_modes: Optional[np.ndarray] = None,
+                     rows: Optional[Sequence[int]] = None) -> Report:
+    """One reuse depth by the head-union page route on the GPU (compaction,
+    then the dense decode over the compacted table, whose finish counts data
+    errors) against ``O.run_page_union_call``: compacted tables and contexts
+    exact, outputs within tolerance, fallback and error counts exact, the
+    support state untouched."""
+    import torch
+    R, H = li.q.shape[:2]
+    required = w.discoveries if required is None else required
+    rows = list(range(R)) if rows is None else list(rows)
+    sup0 = state.support_numpy().copy()
+    tags_raw0 = state.tags.clone()
+    tags0 = state.tags_numpy()
+    ctr0 = state.counters.cpu().numpy().copy()
+    rm_dev = None
+    if row_modes is not None:
+        rm_dev = torch.from_numpy(row_modes.astype(np.uint8)).to(dev.q.device)
+    pu = harness.PageUnion(dev)
+    pu.compact(state, layer_idx=layer, required=required, row_mode=rm_dev)
+    pu.attend(ws, state, layer_idx=layer)
+    torch.cuda.synchronize()
+    slot_of_row = None if state.slot_of_row is None else state.slot_of_row.cpu().numpy()
+    ref = O.run_page_union_call(q=li.q, k_cache=li.k, v_cache=li.v, block_table=li.block_table,
+                                ctx_len=li.ctx_len, page_size=w.page_size, num_pages=li.num_pages,
+                                max_ctx=w.max_ctx, support=sup0, tags=tags0, layer=layer,
+                                slot_of_row=slot_of_row, row_request=state.row_request.cpu().numpy(),
+                                row_position=state.row_position.cpu().numpy(), required=required,
+                                row_modes=row_modes, rows=rows)
+    ctx = pu.ctx.cpu().numpy()
+    bt = pu.bt.cpu().numpy()
+    out = dev.out.cpu().numpy()
+    rep = Report(units=len(rows) * H)
+    for r in rows:
+        assert int(ctx[r]) == int(ref.ctx[r]), f"row {r}: compacted context {ctx[r]} vs {ref.ctx[r]}"
+        if r in ref.tables:
+            k = len(ref.tables[r])
+            assert bt[r, :k].tolist() == ref.tables[r].tolist(), f"row {r}: compacted table"
+        assert_close(out[r], ref.out[r], w.dtype, f"row {r} output", rep)
+    rep.counters = state.counters.cpu().numpy() - ctr0
+    assert np.array_equal(state.support_numpy(), sup0), "support touched"
+    assert torch.equal(state.tags, tags_raw0), "tags touched"
+    if len(rows) == R:
+        assert rep.counters[W.CTR_FALLBACKS] == ref.counters[0]
+        assert rep.counters[W.CTR_ERRORS] == ref.counters[3]
+    rep.page_density = (float(sum(len(ref.pages[r]) for r in rows if r in ref.pages)) /
+                        max(1, sum(-(-int(li.ctx_len[r]) // w.page_size) for r in rows if r in ref.pages)))
     return rep

@@ -161,3 +161,23 @@ def test_lse_route_validation(lib):
     # the other entry points still need V and out
     assert call(lib, "dense", good_attn(v_cache=None)) == W.WISE_E_ARG
     assert call(lib, "finish", good_attn(out=None)) == W.WISE_E_ARG
+
+
+def test_compact_pages_validation(lib):
+    """wise_compact_pages: outputs required, 4-byte aligned, wide enough, and
+    never the input table or contexts (every case fails before a launch)."""
+    a, s = good_attn(), good_support()
+    B, C = FAKE + 4096, FAKE + 8192
+
+    def cp(a=a, s=s, bt=B, stride=4, ctx=C):
+        return lib.wise_compact_pages(ctypes.byref(a), None if s is None else ctypes.byref(s), None,
+                                      bt, stride, ctx, None)
+    assert cp(bt=None) == W.WISE_E_ARG
+    assert cp(ctx=None) == W.WISE_E_ARG
+    assert cp(bt=B + 2) == W.WISE_E_ARG
+    assert cp(stride=3) == W.WISE_E_ARG                 # ceil(64 / 16) = 4 pages needed
+    assert cp(bt=FAKE) == W.WISE_E_ARG                  # the input block table itself
+    assert cp(ctx=FAKE) == W.WISE_E_ARG                 # the input contexts themselves
+    assert cp(s=None) == W.WISE_E_ARG
+    assert cp(s=good_support(words=0)) == W.WISE_E_ARG
+    assert cp(a=good_attn(page_size=12)) == W.WISE_E_UNSUPPORTED
