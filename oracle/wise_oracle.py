@@ -571,6 +571,41 @@ def run_page_union_call(*, q, k_cache, v_cache, block_table, ctx_len, page_size:
     return PageUnionResult(out, tables, ctx_out, counters, kept)
 
 
+# ----------------------------------------------------------------------------
+# O11 support snapshot and restore across a KV offload: the review's first
+#     finding asks for the support and tags of a request to be saved with
+#     its KV and recurrent state and restored on resume, so that reuse after
+#     the resume continues instead of failing.  A record holds one slot's
+#     support words of every (layer, head) and its tag of every layer.
+# ----------------------------------------------------------------------------
+
+def snapshot_slots(support: np.ndarray, tags: np.ndarray, slots: Sequence[int]):
+    """Records of the given slots: (support [layers, heads, words], tags
+    [layers]) copies; a slot out of range gives an empty record (zero words,
+    zero tags, so that reuse from it falls back)."""
+    recs = []
+    for sl in slots:
+        if 0 <= sl < support.shape[0]:
+            recs.append((support[sl].copy(), tags[sl].copy()))
+        else:
+            recs.append((np.zeros(support.shape[1:], support.dtype), np.zeros(tags.shape[1:], tags.dtype)))
+    return recs
+
+
+def restore_slots(support: np.ndarray, tags: np.ndarray, slots: Sequence[int], recs):
+    """Support and tags with record i written into slot slots[i] (new copies).
+    A destination out of range is skipped and counted as a data error."""
+    sup, tg = support.copy(), tags.copy()
+    errors = 0
+    for sl, (words, t) in zip(slots, recs):
+        if 0 <= sl < sup.shape[0]:
+            sup[sl] = words
+            tg[sl] = t
+        else:
+            errors += 1
+    return sup, tg, errors
+
+
 def density(counters: Sequence[int]) -> float:
     """Reuse-union support density: selected blocks over causal blocks."""
     return float(counters[1]) / float(counters[2]) if counters[2] else 0.0

@@ -556,6 +556,46 @@ def test_page_union_call():
     assert r2.pages[0].tolist() == [1] and r2.ctx[0] == 256
 
 
+# ----------------------------------------------------------------------------- O11 snapshot / restore
+
+def test_snapshot_restore_resumes_reuse():
+    """Discovery, offload (snapshot, then the slot is released and reused by
+    another request), resume into another slot (restore): the reuse depth
+    runs sparse with no fallback and gives exactly the never-offloaded
+    output; without the restore it falls back to dense."""
+    rng = np.random.default_rng(61)
+    case, Kl, Vl = paged_case(rng, 150, H=2)
+    sup, tags = state(slots=3, heads=2)
+    common = dict(layer=0, row_request=[7], row_position=[42], required=1, eta=0.9)
+    c = O.run_call(**case, modes=[O.DISCOVER], support=sup, tags=tags, **common)
+    never = O.run_call(**case, modes=[O.SPARSE], support=c.support, tags=c.tags, **common)
+    assert never.counters[0] == 0
+    recs = O.snapshot_slots(c.support, c.tags, [0])
+    # offload: slot 0 released, then taken by another request's discovery
+    freed_sup, freed_tags = c.support.copy(), c.tags.copy()
+    freed_sup[0] = 0
+    freed_tags[0] = np.zeros((), O.TAG_DTYPE)
+    other = O.run_call(**case, modes=[O.DISCOVER], support=freed_sup, tags=freed_tags,
+                       **dict(common, row_request=[8]))
+    # resume into slot 2
+    sup2, tags2, err = O.restore_slots(other.support, other.tags, [2], recs)
+    assert err == 0 and np.array_equal(sup2[2], c.support[0]) and sup2[2].any()
+    assert np.array_equal(sup2[0], other.support[0])          # the other request is untouched
+    resumed = O.run_call(**case, modes=[O.SPARSE], support=sup2, tags=tags2, slot_of_row=[2], **common)
+    assert resumed.counters[0] == 0
+    assert np.array_equal(resumed.out, never.out)
+    # no restore: the resumed request finds no discovery for its token and runs dense
+    lost = O.run_call(**case, modes=[O.SPARSE], support=other.support, tags=other.tags,
+                      slot_of_row=[2], **common)
+    dense = O.run_call(**case, modes=[O.DENSE])
+    assert lost.counters[0] == 1 and np.array_equal(lost.out, dense.out)
+    # a record of a slot out of range is empty; a destination out of range is an error
+    empty = O.snapshot_slots(c.support, c.tags, [5])[0]
+    assert not empty[0].any() and int(empty[1]["discoveries"][0]) == 0
+    _, _, err = O.restore_slots(c.support, c.tags, [3], recs)
+    assert err == 1
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def test_pins_catch_planted_mistakes(monkeypatch):
