@@ -236,6 +236,8 @@ def main():
                     help="skip the timing of discovery by the LSE route")
     ap.add_argument("--no-page-route", action="store_true",
                     help="skip the timing of the head-union page route")
+    ap.add_argument("--no-state-copy", action="store_true",
+                    help="skip the timing of the support/tag snapshot and restore")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (for counter-collection runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -459,6 +461,32 @@ def main():
             if "dense_same_kv" in modes_out:
                 entry["speedup_vs_dense"] = round(modes_out["dense_same_kv"]["split_us"] / total_us, 3)
             modes_out["page_union"] = entry
+
+    # ---- support/tag snapshot and restore of every row's slot (KV offload and resume) ----
+    if not args.no_state_copy:
+        st_ = plan.state
+        slots = torch.arange(w.rows, dtype=torch.int32, device=dev)
+        rec = st_.record_bytes()
+        records = torch.empty(w.rows * rec, dtype=torch.uint8, device=dev)
+        n_it = 20
+        ev5 = harness.HipEvents(4 * n_it)
+        st_.snapshot(slots, records, sh)
+        st_.restore(slots, records, sh)
+        for it in range(n_it):
+            ev5.record(4 * it, sh)
+            st_.snapshot(slots, records, sh)
+            ev5.record(4 * it + 1, sh)
+            ev5.record(4 * it + 2, sh)
+            st_.restore(slots, records, sh)
+            ev5.record(4 * it + 3, sh)
+        torch.cuda.synchronize()
+        snap_ms = np.mean([ev5.elapsed_ms(4 * it, 4 * it + 1) for it in range(n_it)])
+        rest_ms = np.mean([ev5.elapsed_ms(4 * it + 2, 4 * it + 3) for it in range(n_it)])
+        modes_out["offload_state"] = {"snapshot_us": round(float(snap_ms) * 1e3, 2),
+                                      "restore_us": round(float(rest_ms) * 1e3, 2),
+                                      "bytes_per_slot": rec, "slots": w.rows,
+                                      "note": "support words of every layer and head + tags, all rows' "
+                                              "slots; each copy reads and writes slots x bytes_per_slot"}
 
     rows_per_step = w.rows * calls
     out = {

@@ -10,7 +10,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = ["wise_api.hip", "wise_split.hip", "wise_finish.hip", "wise_pages.hip"]
+SOURCES = ["wise_api.hip", "wise_split.hip", "wise_finish.hip", "wise_pages.hip", "wise_state.hip"]
 LIB = os.path.join(PKG, "libwise.so")
 ARCH = "gfx950"
 

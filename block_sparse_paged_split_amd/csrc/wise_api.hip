@@ -336,6 +336,48 @@ wise_status wise_compact_pages(const wise_attn *a, const wise_support *s, const 
   return WISE_OK;
 }
 
+size_t wise_snapshot_bytes(int32_t layers, int32_t heads, int32_t words) {
+  if (layers < 1 || heads < 1 || words < 1) return 0;
+  size_t off = 0, bytes = 0;
+  state_record_layout(layers, heads, words, &off, &bytes);
+  return bytes;
+}
+
+static wise_status state_copy(const wise_support *s, int32_t heads, const int32_t *slots, int32_t count,
+                              void *records, size_t bytes, bool restore, void *stream) {
+  if (!s || !s->support || !s->tags || !slots || !records) return WISE_E_ARG;
+  if (s->slots < 1 || s->layers < 1 || s->words < 1 || heads < 1 || count < 0) return WISE_E_ARG;
+  if (!aligned(s->support, 4) || !aligned(s->tags, 8) || !aligned(slots, 4) || !aligned(records, 8) ||
+      (s->counters && !aligned(s->counters, 8)))
+    return WISE_E_ARG;
+  StateParams p{};
+  state_record_layout(s->layers, heads, s->words, &p.tags_offset, &p.record_bytes);
+  if (bytes < p.record_bytes * static_cast<size_t>(count)) return WISE_E_ARG;
+  if (count == 0) return WISE_OK;
+  p.support = s->support;
+  p.tags = s->tags;
+  p.slots = s->slots;
+  p.layers = s->layers;
+  p.heads = heads;
+  p.words = s->words;
+  p.slots_list = slots;
+  p.count = count;
+  p.records = records;
+  p.counters = reinterpret_cast<unsigned long long *>(s->counters);
+  if (launch_state_copy(p, restore, static_cast<hipStream_t>(stream)) != hipSuccess) return WISE_E_HIP;
+  return WISE_OK;
+}
+
+wise_status wise_support_snapshot(const wise_support *s, int32_t heads, const int32_t *slots, int32_t count,
+                                  void *dst, size_t dst_bytes, void *stream) {
+  return state_copy(s, heads, slots, count, dst, dst_bytes, false, stream);
+}
+
+wise_status wise_support_restore(const wise_support *s, int32_t heads, const int32_t *slots, int32_t count,
+                                 const void *src, size_t src_bytes, void *stream) {
+  return state_copy(s, heads, slots, count, const_cast<void *>(src), src_bytes, true, stream);
+}
+
 const char *wise_status_string(wise_status st) {
   switch (st) {
     case WISE_OK: return "ok";

@@ -112,6 +112,20 @@ struct PageParams {
   int32_t *ctx_out;
 };
 
+// Snapshot (support, tags of listed slots -> records) or restore (records ->
+// slots); see wise_state.hip for the record layout.
+struct StateParams {
+  uint32_t *support;
+  wise_tag *tags;
+  int32_t slots, layers, heads, words;
+  const int32_t *slots_list;  // [count] slot of each record
+  int32_t count;
+  void *records;
+  size_t record_bytes, tags_offset;
+  unsigned long long *counters;
+};
+void state_record_layout(int layers, int heads, int words, size_t *tags_offset, size_t *record_bytes);
+
 // listed = plan kernel + persistent split over the compact item list (calls
 // with sparse rows); otherwise the static one-wave-per-item-slot grid.
 // k_only = read K only and keep tile stats (static grid, discovery modes).
@@ -121,5 +135,6 @@ hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool list
                         hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_finish(const FinishParams &p, hipStream_t stream);
 hipError_t launch_compact_pages(const PageParams &p, hipStream_t stream);
+hipError_t launch_state_copy(const StateParams &p, bool restore, hipStream_t stream);
 
 }  // namespace wise

@@ -104,6 +104,22 @@ class SupportState:
     def support_numpy(self):
         return self.support.cpu().numpy().view(np.uint32)
 
+    def record_bytes(self) -> int:
+        layers, heads = self.support.shape[1], self.support.shape[2]
+        return W.wise_snapshot_bytes(layers, heads, self.words)
+
+    def snapshot(self, slots, records, stream: Optional[int] = None) -> None:
+        """Records of the given slots (device int32 tensor) into ``records``
+        (device uint8 tensor of len(slots) * record_bytes())."""
+        st = stream_handle() if stream is None else stream
+        W.wise_support_snapshot(self.view(0, 1, 0.95), self.support.shape[2], int(slots.data_ptr()),
+                                int(slots.numel()), int(records.data_ptr()), int(records.numel()), st)
+
+    def restore(self, slots, records, stream: Optional[int] = None) -> None:
+        st = stream_handle() if stream is None else stream
+        W.wise_support_restore(self.view(0, 1, 0.95), self.support.shape[2], int(slots.data_ptr()),
+                               int(slots.numel()), int(records.data_ptr()), int(records.numel()), st)
+
 
 class Workspace:
     def __init__(self, rows, heads, head_dim, max_ctx, device="cuda"):

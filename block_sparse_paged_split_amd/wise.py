@@ -26,7 +26,7 @@ BLOCK = 32
 
 EXPORTED = ("wise_workspace_size", "wise_decode_dense", "wise_decode_discover",
             "wise_decode_sparse", "wise_finish_select", "wise_discover_lse", "wise_compact_pages",
-            "wise_status_string")
+            "wise_snapshot_bytes", "wise_support_snapshot", "wise_support_restore", "wise_status_string")
 
 
 class WiseTag(ctypes.Structure):
@@ -82,8 +82,13 @@ def lib() -> ctypes.CDLL:
         L.wise_finish_select.argtypes = [P, S, V, ctypes.c_size_t, V]
         L.wise_discover_lse.argtypes = [P, S, ctypes.c_int32, V, V, ctypes.c_size_t, V]
         L.wise_compact_pages.argtypes = [P, S, V, V, ctypes.c_int32, V, V]
+        L.wise_snapshot_bytes.restype = ctypes.c_size_t
+        L.wise_snapshot_bytes.argtypes = [ctypes.c_int32] * 3
+        L.wise_support_snapshot.argtypes = [S, ctypes.c_int32, V, ctypes.c_int32, V, ctypes.c_size_t, V]
+        L.wise_support_restore.argtypes = [S, ctypes.c_int32, V, ctypes.c_int32, V, ctypes.c_size_t, V]
         for f in ("wise_decode_dense", "wise_decode_discover", "wise_decode_sparse",
-                  "wise_finish_select", "wise_discover_lse", "wise_compact_pages"):
+                  "wise_finish_select", "wise_discover_lse", "wise_compact_pages",
+                  "wise_support_snapshot", "wise_support_restore"):
             getattr(L, f).restype = ctypes.c_int
         L.wise_status_string.restype = ctypes.c_char_p
         L.wise_status_string.argtypes = [ctypes.c_int]
@@ -142,6 +147,22 @@ def wise_compact_pages(a: WiseAttn, s: WiseSupport, row_mode: Optional[int], bt_
                        bt_out_stride: int, ctx_out: int, stream: int = 0) -> None:
     _check(lib().wise_compact_pages(ctypes.byref(a), ctypes.byref(s), row_mode, bt_out, bt_out_stride,
                                     ctx_out, stream), "wise_compact_pages")
+
+
+def wise_snapshot_bytes(layers: int, heads: int, words: int) -> int:
+    return int(lib().wise_snapshot_bytes(layers, heads, words))
+
+
+def wise_support_snapshot(s: WiseSupport, heads: int, slots: int, count: int, dst: int, dst_bytes: int,
+                          stream: int = 0) -> None:
+    _check(lib().wise_support_snapshot(ctypes.byref(s), heads, slots, count, dst, dst_bytes, stream),
+           "wise_support_snapshot")
+
+
+def wise_support_restore(s: WiseSupport, heads: int, slots: int, count: int, src: int, src_bytes: int,
+                         stream: int = 0) -> None:
+    _check(lib().wise_support_restore(ctypes.byref(s), heads, slots, count, src, src_bytes, stream),
+           "wise_support_restore")
 
 
 # ----------------------------------------------------------------------------- torch marshalling

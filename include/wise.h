@@ -244,6 +244,42 @@ wise_status wise_compact_pages(const wise_attn *a, const wise_support *s,
                                const uint8_t *row_mode, int32_t *bt_out,
                                int32_t bt_out_stride, int32_t *ctx_out, void *stream);
 
+/*
+ * Support/tag snapshot and restore across a KV offload (WISE pull request
+ * page, review finding "Preserve WISE state across KV offload": freeing a
+ * request for offload after its discovery depths loses its support and
+ * tags; the finding asks to snapshot and restore them with the recurrent
+ * state).  A record holds one slot's support words of every layer and head
+ * and its tag of every layer; a restored tag names the same (request,
+ * position), so a request resumed at the same token continues its sparse
+ * reuse instead of falling back to dense.
+ *
+ * wise_snapshot_bytes: bytes of one record (0 if an argument is < 1).
+ *   Layout: [layers][heads][words] uint32 support words, padded to a
+ *   multiple of 8 bytes, then [layers] wise_tag.
+ * wise_support_snapshot: record i <- slot slots[i] (i < count).  A slot
+ *   outside [0, s->slots) yields an all-zero record (restoring it makes the
+ *   slot's reuse fall back).
+ * wise_support_restore: slot slots[i] <- record i.  A slot outside
+ *   [0, s->slots) is skipped and counted in s->counters[WISE_CTR_ERRORS].
+ *   Destination slots must be distinct and must not be read or written by
+ *   other work in flight.
+ *   s         support state: support, tags, slots, layers, words, counters
+ *             (the other fields are not read).
+ *   heads     heads per (slot, layer) of the support array.
+ *   slots     [count] int32 device array; count >= 0 (0 enqueues nothing).
+ *   dst/src   device (or device-accessible pinned host) buffer of
+ *             dst_bytes/src_bytes >= count * wise_snapshot_bytes(...),
+ *             8-byte aligned, caller-owned.
+ * WISE_E_ARG for a null or misaligned pointer, sizes < 1, or a buffer too
+ * small.  One kernel launch each; nothing allocated, nothing synchronised.
+ */
+size_t wise_snapshot_bytes(int32_t layers, int32_t heads, int32_t words);
+wise_status wise_support_snapshot(const wise_support *s, int32_t heads, const int32_t *slots,
+                                  int32_t count, void *dst, size_t dst_bytes, void *stream);
+wise_status wise_support_restore(const wise_support *s, int32_t heads, const int32_t *slots,
+                                 int32_t count, const void *src, size_t src_bytes, void *stream);
+
 /* Static, human-readable name of a status. */
 const char *wise_status_string(wise_status st);
 

@@ -181,3 +181,28 @@ def test_compact_pages_validation(lib):
     assert cp(s=None) == W.WISE_E_ARG
     assert cp(s=good_support(words=0)) == W.WISE_E_ARG
     assert cp(a=good_attn(page_size=12)) == W.WISE_E_UNSUPPORTED
+
+
+def test_snapshot_bytes_and_validation(lib):
+    # [layers][heads][words] uint32 padded to 8 bytes, then [layers] 24-byte tags
+    assert W.wise_snapshot_bytes(24, 16, 4) == 24 * 16 * 4 * 4 + 24 * 24
+    assert W.wise_snapshot_bytes(1, 3, 1) == 16 + 24
+    assert W.wise_snapshot_bytes(0, 16, 4) == 0 and W.wise_snapshot_bytes(1, 1, 0) == 0
+    s = good_support(layers=2, words=1)
+    need = W.wise_snapshot_bytes(2, 2, 1)
+    D = FAKE + 4096
+
+    def snap(s=s, heads=2, slots=FAKE, count=3, dst=D, nbytes=3 * need):
+        return lib.wise_support_snapshot(None if s is None else ctypes.byref(s), heads, slots, count, dst,
+                                         nbytes, None)
+    assert snap(s=None) == W.WISE_E_ARG
+    assert snap(slots=None) == W.WISE_E_ARG
+    assert snap(dst=None) == W.WISE_E_ARG
+    assert snap(dst=D + 4) == W.WISE_E_ARG              # records are 8-byte aligned
+    assert snap(nbytes=3 * need - 1) == W.WISE_E_ARG
+    assert snap(heads=0) == W.WISE_E_ARG
+    assert snap(count=-1) == W.WISE_E_ARG
+    assert snap(s=good_support(tags=None)) == W.WISE_E_ARG
+    assert snap(count=0, nbytes=0) == W.WISE_OK         # nothing to copy, nothing enqueued
+    assert lib.wise_support_restore(ctypes.byref(s), 2, FAKE, 3, D, 3 * need - 8, None) == W.WISE_E_ARG
+    assert lib.wise_support_restore(ctypes.byref(s), 2, FAKE, 0, D, 0, None) == W.WISE_OK
