@@ -417,7 +417,7 @@ def main():
                    for _, depth, layer in sparse_keys]
             for pu, layer in pus:
                 pu.compact(plan.state, layer, w.discoveries, stream=sh)
-                pu.attend(plan.ws, None, layer, stream=sh)
+                pu.attend(plan.ws, stream=sh)
             n_it = max(20, 2 * len(pus))
             ev4 = harness.HipEvents(4 * n_it + 2)
             L = W.lib()

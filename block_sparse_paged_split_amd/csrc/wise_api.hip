@@ -185,7 +185,9 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
     p.row_request = s->row_request;
     p.row_position = s->row_position;
     p.counters = reinterpret_cast<unsigned long long *>(s->counters);
+    p.eta = s->eta;
   }
+  p.out = a->out;
   p.row_code = reinterpret_cast<int32_t *>(w + L.off_row_code);
   p.row_done = reinterpret_cast<unsigned long long *>(w + L.off_row_done);
   p.unit_items = reinterpret_cast<int32_t *>(w + L.off_unit_items);
@@ -202,10 +204,14 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
   // over the compact item list; otherwise the static grid has one workgroup
   // per unit and no empty slots worth removing.
   const bool listed = (row_mode != nullptr || uniform_mode == WISE_SPARSE) && p.chunk_groups > 1;
+  // units that fit one split workgroup are also finished by it (the paired
+  // wise_finish_select then has nothing left to do)
+  const bool fused = !k_only && fused_finish_shape(L, a->heads);
   const int cus = listed ? compute_units() : 0;
   if (listed && cus <= 0) return WISE_E_HIP;
-  if (launch_split(p, a->dtype, a->head_dim, listed, k_only, cus, static_cast<hipEvent_t>(a->ev_split_begin),
-                   static_cast<hipEvent_t>(a->ev_split_end), strm) != hipSuccess)
+  if (launch_split(p, a->dtype, a->head_dim, listed, k_only, fused, cus,
+                   static_cast<hipEvent_t>(a->ev_split_begin), static_cast<hipEvent_t>(a->ev_split_end),
+                   strm) != hipSuccess)
     return WISE_E_HIP;
   return WISE_OK;
 }
@@ -221,6 +227,8 @@ wise_status finish(const wise_attn *a, const wise_support *s, const float *lse, 
   }
   st = check_ws(ws, ws_bytes, L);
   if (st != WISE_OK) return st;
+  // the decode call already finished these units (see decode())
+  if (lse == nullptr && fused_finish_shape(L, a->heads)) return WISE_OK;
   char *w = static_cast<char *>(ws);
   FinishParams p{};
   p.rows = a->rows;
@@ -314,6 +322,7 @@ wise_status wise_compact_pages(const wise_attn *a, const wise_support *s, const 
   p.heads = a->heads;
   p.max_ctx = a->max_ctx;
   p.page_shift = log2i(a->page_size);
+  p.num_pages = a->num_pages;
   p.block_table = a->block_table;
   p.bt_stride = a->bt_stride;
   p.ctx_len = a->ctx_len;

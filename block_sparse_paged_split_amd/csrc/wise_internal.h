@@ -50,13 +50,17 @@ struct SplitParams {
   // requested modes
   const uint8_t *row_mode;  // NULL: every row uniform_mode
   int32_t uniform_mode;
-  // support state (unused when every row is DENSE)
-  const uint32_t *support;
+  // support state (unused when every row is DENSE); written only by the
+  // fused split + finish kernel
+  uint32_t *support;
   int32_t slots, layers, layer, words, required;
   const int32_t *slot_of_row;
-  const wise_tag *tags;
+  wise_tag *tags;
   const int64_t *row_request, *row_position;
   unsigned long long *counters;
+  // fused split + finish only: the output and the selection target
+  float *out;
+  float eta;
   // workspace and optional export
   int32_t *row_code, *unit_items;
   unsigned long long *row_done;
@@ -96,7 +100,7 @@ struct FinishParams {
 
 // Head-union page compaction of one reuse depth (see wise_pages.hip).
 struct PageParams {
-  int32_t rows, heads, max_ctx, page_shift;
+  int32_t rows, heads, max_ctx, page_shift, num_pages;
   const int32_t *block_table;
   int32_t bt_stride;
   const int32_t *ctx_len;
@@ -129,10 +133,20 @@ void state_record_layout(int layers, int heads, int words, size_t *tags_offset, 
 // listed = plan kernel + persistent split over the compact item list (calls
 // with sparse rows); otherwise the static one-wave-per-item-slot grid.
 // k_only = read K only and keep tile stats (static grid, discovery modes).
+// fused = static grid of one workgroup per unit that also runs the unit's
+// finish (merge, selection, support, row bookkeeping).
 // cus = compute units of the current device (sizes the persistent grid);
 // ev_begin / ev_end (optional) are recorded right around the split kernel.
-hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, int cus,
-                        hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
+hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, bool fused,
+                        int cus, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
+
+// The finish is fused into the split kernel when every unit's items fit one
+// split workgroup (one wave per item) and a row's heads fit the 8-bit
+// arrival count kept in the tag's reserved word.  Decode and finish calls
+// take the same decision from the same sizes.
+inline bool fused_finish_shape(const Layout &L, int heads) {
+  return L.items_per_unit <= kWavesPerGroup && heads <= 255;
+}
 hipError_t launch_finish(const FinishParams &p, hipStream_t stream);
 hipError_t launch_compact_pages(const PageParams &p, hipStream_t stream);
 hipError_t launch_state_copy(const StateParams &p, bool restore, hipStream_t stream);

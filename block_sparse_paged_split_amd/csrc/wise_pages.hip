@@ -18,7 +18,10 @@
 //  * the compacted context is (kept - 1) * P + the valid tokens of the last
 //    kept page: only the context's last page can be partial, and it can
 //    only be the last one kept.
-// The attention itself is any paged dense decode over (bt_out, ctx_out).
+// Rows with bad data (another mode, a context outside [1, max_ctx], a slot
+// out of range, an empty union, a kept page id out of range) get context 0
+// and count one error per head here.  The attention itself is any paged
+// dense decode over (bt_out, ctx_out).
 #include "wise_internal.h"
 
 namespace wise {
@@ -58,23 +61,24 @@ __global__ __launch_bounds__(64 * kPageWaves) void compact_pages_kernel(const Pa
   const int slot_in = p.slot_of_row ? p.slot_of_row[r] : r;
   int32_t *dst = p.bt_out + static_cast<int64_t>(r) * p.bt_out_stride;
   const int32_t *src = p.block_table + static_cast<int64_t>(r) * p.bt_stride;
-  // rows the attention call must flag: another mode (context 0), a bad context (kept as is)
-  if (req != WISE_DENSE && req != WISE_SPARSE) {
-    if (lane == 0) p.ctx_out[r] = 0;
-    return;
-  }
-  if (n < 1 || n > p.max_ctx) {
-    if (lane == 0) p.ctx_out[r] = n;
+  // a row with bad data gets context 0 (the attention call writes NaN for
+  // it) and one error per head
+  auto row_error = [&]() {
+    if (lane == 0) {
+      p.ctx_out[r] = 0;
+      if (p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, static_cast<unsigned long long>(p.heads));
+    }
+  };
+  if ((req != WISE_DENSE && req != WISE_SPARSE) || n < 1 || n > p.max_ctx) {
+    row_error();
     return;
   }
   const int P = 1 << p.page_shift;
   const int npg = (n + P - 1) >> p.page_shift;
   const int slot = req == WISE_SPARSE ? slot_in : r;
-  if (req == WISE_SPARSE) {
-    if (slot < 0 || slot >= p.slots) {
-      if (lane == 0) p.ctx_out[r] = 0;
-      return;
-    }
+  if (req == WISE_SPARSE && (slot < 0 || slot >= p.slots)) {
+    row_error();
+    return;
   }
   // Issued together, before anything waits: the first kChunkBatch steps of
   // the block table, the tag, and the support words of every head (lane w
@@ -120,6 +124,7 @@ __global__ __launch_bounds__(64 * kPageWaves) void compact_pages_kernel(const Pa
   // pages per step; the table entries of kChunkBatch steps are loaded before
   // the first of them is compacted
   int count = 0, last = -1;
+  bool bad_page = false;
   for (int c0 = 0; c0 < npg; c0 += 64 * kChunkBatch) {
     if (c0 > 0) {
 #pragma unroll
@@ -143,13 +148,18 @@ __global__ __launch_bounds__(64 * kPageWaves) void compact_pages_kernel(const Pa
       const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0));
       if (keep) dst[count + rank] = ids[t];
+      bad_page |= keep && static_cast<unsigned>(ids[t]) >= static_cast<unsigned>(p.num_pages);
       if (bm) last = j0 + 63 - __builtin_clzll(bm);
       count += __popcll(bm);
     }
   }
-  // an empty union is a data error the attention call flags (context 0);
+  // an empty union and a kept page id out of range are data errors;
   // keeping every page gives back n
-  if (lane == 0) p.ctx_out[r] = count == 0 ? 0 : (count - 1) * P + min(P, n - last * P);
+  if (count == 0 || __builtin_amdgcn_ballot_w64(bad_page) != 0ull) {
+    row_error();
+    return;
+  }
+  if (lane == 0) p.ctx_out[r] = (count - 1) * P + min(P, n - last * P);
 }
 
 }  // namespace

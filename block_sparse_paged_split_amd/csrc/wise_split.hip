@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "wise_internal.h"
+#include "wise_select.h"
 
 namespace wise {
 
@@ -148,12 +149,13 @@ __device__ __forceinline__ u32x4 load16(const char *p) {
 // Planning of one row: effective mode from the support tags, dense fallback.
 // ---------------------------------------------------------------------------
 struct RowPlan {
-  int n, req, eff, slot;
+  int row, n, req, eff, slot;
   bool bad, fallback;
 };
 
 __device__ __forceinline__ RowPlan plan_row(const SplitParams &p, int r) {
   RowPlan rp;
+  rp.row = r;
   rp.n = p.ctx_len[r];
   rp.req = p.row_mode ? static_cast<int>(p.row_mode[r]) : p.uniform_mode;
   rp.bad = rp.n < 1 || rp.n > p.max_ctx || rp.req < WISE_DENSE || rp.req > WISE_SPARSE;
@@ -205,9 +207,18 @@ __device__ __forceinline__ int support_scan(const SplitParams &p, int slot, int 
 // scores' tile stats and (m, l) are kept, V and the accumulator are not
 // (discovery after an external dense kernel).
 // ---------------------------------------------------------------------------
+// Where one item's results go when the finish is fused into the split
+// kernel: LDS of the unit's workgroup instead of the workspace.
+struct UnitLds {
+  float *acc;       // [items][D] partial accumulators
+  float2 *ml;       // [items] partial (m, l); l < 0 marks a bad page
+  float2 *stats;    // [blocks] tile stats by block index (non-sparse items)
+};
+
 template <bool kBf16, int D, bool kKOnly>
 __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int h, int k, int n, bool sparse,
-                                         int count, uint32_t word, int incl, int lane, int *tiles) {
+                                         int count, uint32_t word, int incl, int lane, int *tiles,
+                                         const UnitLds *lds = nullptr) {
   using G = Geo<kBf16, D>;
   const int T = p.tiles_per_item;
   const int first = k * T;
@@ -336,16 +347,30 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
 #pragma unroll
     for (int e = 0; e < G::EPL; ++e) acc[e] = subgroup_sum<G::LPT>(acc[e]);
   }
-  if (!kKOnly && g == 0) {
-    float4 *dst = reinterpret_cast<float4 *>(p.part_acc + slot_idx * D + c * G::EPL);
+  const float2 ml = page_err ? make_float2(0.0f, -1.0f) : make_float2(m_run, l_run);
+  if (lds) {
+    if (!kKOnly && g == 0) {
+      float4 *dst = reinterpret_cast<float4 *>(lds->acc + k * D + c * G::EPL);
 #pragma unroll
-    for (int e = 0; e < G::EPL; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      for (int e = 0; e < G::EPL; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
+    if (lane == 0) lds->ml[k] = ml;
+  } else {
+    if (!kKOnly && g == 0) {
+      float4 *dst = reinterpret_cast<float4 *>(p.part_acc + slot_idx * D + c * G::EPL);
+#pragma unroll
+      for (int e = 0; e < G::EPL; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
+    if (lane == 0) p.part_ml[slot_idx] = ml;
   }
-  if (lane == 0) p.part_ml[slot_idx] = page_err ? make_float2(0.0f, -1.0f) : make_float2(m_run, l_run);
   if (lane < ntiles) {
     const int b = sparse ? tiles[lane] : first + lane;
     const int64_t si = static_cast<int64_t>(u) * p.max_blocks + b;
-    p.stats[si] = make_float2(st_m, st_l);
+    if (lds) {
+      if (!sparse) lds->stats[b] = make_float2(st_m, st_l);
+    } else {
+      p.stats[si] = make_float2(st_m, st_l);
+    }
     if (p.stats_export) p.stats_export[si] = make_float2(st_m * kLn2, st_l);
   }
 }
@@ -398,6 +423,124 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
   }
   if (k >= items) return;
   run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave]);
+}
+
+// ---------------------------------------------------------------------------
+// Fused split + finish, for calls whose units fit one workgroup each (one
+// wave per item): the items leave their partials and tile stats in LDS, and
+// wave 0 then finishes the unit as the finish kernel would -- the same merge
+// in the same order (so the output bits do not depend on which kernel ran
+// it), the eta selection, the support write or OR.  A discovery row's tag and
+// the density counters are updated by the last of its heads to arrive,
+// counted in the tag's reserved word (arrivals | error heads << 8 | newly
+// selected blocks << 16), which that last arrival returns to zero.  Every
+// unit of the row planned from the tag before any head arrives, so the
+// update cannot race with a plan.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan &rp, int u, int h, int nb,
+                                             int items, const float *s_acc, const float2 *s_ml,
+                                             const float2 *s_st, float *s_w, uint32_t *s_bits, int lane) {
+  const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
+  const bool discover = stateful && (rp.eff == WISE_DISCOVER || rp.eff == WISE_DISCOVER_UNION);
+  // merge: M = max m_i, w_i = 2^(m_i - M), L = sum l_i w_i, out = sum acc_i w_i / L
+  const float2 ml = lane < items ? s_ml[lane] : make_float2(-INFINITY, 0.0f);
+  const float M = sel::wave_max(ml.x);
+  const bool err = items == 0 || __builtin_amdgcn_ballot_w64(ml.y < 0.0f) != 0ull;
+  float Lp = 0.0f;
+  if (lane < items) {
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    s_w[lane] = w;
+    Lp = fmaf(ml.y, w, Lp);
+  }
+  const float L = sel::wave_sum(Lp);
+  if (discover)
+    for (int w = lane; w < kMaxWords; w += 64) s_bits[w] = 0u;
+  sel::wave_lds_sync();
+  for (int dd = lane; dd < D; dd += 64) {
+    float a = 0.0f;
+    for (int t = 0; t < items; ++t) a = fmaf(s_acc[t * D + dd], s_w[t], a);
+    p.out[static_cast<int64_t>(u) * D + dd] = err ? __builtin_nanf("") : a / L;
+  }
+  if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
+  if (!stateful) return;
+  wise_tag *tag = p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer;
+  if (!discover) {
+    // a union row whose discovery window is broken ran dense: the rest of
+    // this token runs dense too
+    if (rp.req == WISE_DISCOVER_UNION && h == 0 && lane == 0) tag->discoveries = 0;
+    return;
+  }
+  int selected = 0;
+  if (!err) {
+    const float2 st[1] = {lane < nb ? s_st[lane] : make_float2(0.0f, 0.0f)};
+    const int K = nb <= 16   ? sel::select_eta<1, 16>(st, p.eta, nb, M, L, lane, s_bits)
+                  : nb <= 32 ? sel::select_eta<1, 32>(st, p.eta, nb, M, L, lane, s_bits)
+                             : sel::select_eta<1, 64>(st, p.eta, nb, M, L, lane, s_bits);
+    sel::wave_lds_sync();
+    uint32_t *sw = p.support + ((static_cast<int64_t>(rp.slot) * p.layers + p.layer) * p.heads + h) * p.words;
+    int added = 0;
+    for (int w = lane; w < p.words; w += 64) {
+      const uint32_t nw = w < kMaxWords ? s_bits[w] : 0u;
+      if (rp.eff == WISE_DISCOVER) {
+        sw[w] = nw;
+      } else {
+        const uint32_t old = sw[w];
+        sw[w] = old | nw;
+        added += __popc(nw & ~old);
+      }
+    }
+    selected = rp.eff == WISE_DISCOVER ? K : sel::wave_sum_int(added);
+  }
+  if (lane != 0) return;
+  unsigned int *arrive = reinterpret_cast<unsigned int *>(&tag->reserved);
+  const unsigned int mine = 1u | (err ? 1u << 8 : 0u) | (static_cast<unsigned int>(selected) << 16);
+  const unsigned int all = atomicAdd(arrive, mine) + mine;
+  if (static_cast<int>(all & 0xFFu) != p.heads) return;
+  atomicExch(arrive, 0u);
+  const int err_heads = static_cast<int>((all >> 8) & 0xFFu);
+  if (p.counters) {
+    atomicAdd(p.counters + WISE_CTR_SELECTED, static_cast<unsigned long long>(all >> 16));
+    if (rp.eff == WISE_DISCOVER)
+      atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(nb) * (p.heads - err_heads));
+  }
+  // a bad page in any head of the row breaks this discovery
+  if (rp.eff == WISE_DISCOVER) {
+    tag->request = p.row_request[rp.row];
+    tag->position = p.row_position[rp.row];
+    tag->discoveries = err_heads ? 0 : 1;
+  } else {
+    tag->discoveries = err_heads ? 0 : tag->discoveries + 1;
+  }
+}
+
+template <bool kBf16, int D>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void split_fused_kernel(const SplitParams p) {
+  __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
+  __shared__ float s_acc[kWavesPerGroup * D];
+  __shared__ float2 s_ml[kWavesPerGroup];
+  __shared__ float2 s_st[kWavesPerGroup * kMaxTilesPerItem];
+  __shared__ float s_w[kWavesPerGroup];
+  __shared__ uint32_t s_bits[kMaxWords];
+  const int lane = threadIdx.x & 63;
+  const int k = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);  // item slot
+  const int u = blockIdx.x;  // unit = (row, head); units of a row spread over the XCDs
+  const int r = u / p.heads;
+  const int h = u - r * p.heads;
+  const RowPlan rp = plan_row(p, r);
+  const int nb = rp.bad ? 0 : (rp.n + kBlock - 1) / kBlock;
+  const bool sparse = !rp.bad && rp.eff == WISE_SPARSE;
+  uint32_t word = 0u;
+  int incl = 0;
+  const int count = sparse ? support_scan(p, rp.slot, h, nb, lane, word, incl) : nb;
+  const int items = (count + p.tiles_per_item - 1) / p.tiles_per_item;
+  if (k == 0 && lane == 0 && h == 0 && rp.fallback && p.counters)
+    atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
+  const UnitLds lds{s_acc, s_ml, s_st};
+  if (k < items)
+    run_item<kBf16, D, false>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], &lds);
+  __syncthreads();  // every wave of the workgroup reaches this once
+  if (k == 0) finish_fused<D>(p, rp, u, h, nb, items, s_acc, s_ml, s_st, s_w, s_bits, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -508,8 +651,8 @@ static int listed_groups_per_cu() {
 }
 
 template <bool kBf16, int D>
-static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, int cus, hipEvent_t ev_begin,
-                               hipEvent_t ev_end, hipStream_t stream) {
+static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, bool fused, int cus,
+                               hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
   const dim3 block(64 * kWavesPerGroup);
   if (listed) {
     const int per_cu = listed_groups_per_cu<kBf16, D>();
@@ -523,7 +666,10 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, i
   } else {
     const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
     if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipErrorInvalidValue;
-    if (k_only)
+    if (fused)
+      hipLaunchKernelGGL((split_fused_kernel<kBf16, D>), dim3(static_cast<unsigned>(p.rows) * p.heads), block, 0,
+                         stream, p);
+    else if (k_only)
       hipLaunchKernelGGL((split_static_kernel<kBf16, D, true>), grid, block, 0, stream, p);
     else
       hipLaunchKernelGGL((split_static_kernel<kBf16, D, false>), grid, block, 0, stream, p);
@@ -534,17 +680,18 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, i
   return hipSuccess;
 }
 
-hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, int cus,
-                        hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
-  if (listed && k_only) return hipErrorInvalidValue;  // K-only calls have no sparse rows
+hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, bool fused,
+                        int cus, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
+  if (listed && (k_only || fused)) return hipErrorInvalidValue;  // K-only and fused calls use the static grid
+  if (fused && (k_only || p.chunk_groups != 1)) return hipErrorInvalidValue;
   if (dtype == WISE_BF16 && head_dim == 128)
-    return launch_typed<true, 128>(p, listed, k_only, cus, ev_begin, ev_end, stream);
+    return launch_typed<true, 128>(p, listed, k_only, fused, cus, ev_begin, ev_end, stream);
   if (dtype == WISE_BF16 && head_dim == 64)
-    return launch_typed<true, 64>(p, listed, k_only, cus, ev_begin, ev_end, stream);
+    return launch_typed<true, 64>(p, listed, k_only, fused, cus, ev_begin, ev_end, stream);
   if (dtype == WISE_F32 && head_dim == 128)
-    return launch_typed<false, 128>(p, listed, k_only, cus, ev_begin, ev_end, stream);
+    return launch_typed<false, 128>(p, listed, k_only, fused, cus, ev_begin, ev_end, stream);
   if (dtype == WISE_F32 && head_dim == 64)
-    return launch_typed<false, 64>(p, listed, k_only, cus, ev_begin, ev_end, stream);
+    return launch_typed<false, 64>(p, listed, k_only, fused, cus, ev_begin, ev_end, stream);
   return hipErrorInvalidValue;
 }
 

@@ -196,13 +196,13 @@ class PageUnion:
         a.ctx_len = int(self.ctx.data_ptr())
         return a
 
-    def attend(self, ws: "Workspace", state: Optional[SupportState] = None, layer_idx: int = 0,
-               events=None, stream: Optional[int] = None) -> None:
+    def attend(self, ws: "Workspace", events=None, stream: Optional[int] = None) -> None:
+        """Dense decode over the compacted table (data errors were counted by
+        the compaction)."""
         st = stream_handle() if stream is None else stream
         a = self.attend_attn(events)
-        s = state.view(layer_idx, 1, 0.95) if state is not None else None
         W.wise_decode_dense(a, ws.ptr, ws.nbytes, st)
-        W.wise_finish_select(a, s, ws.ptr, ws.nbytes, st)
+        W.wise_finish_select(a, None, ws.ptr, ws.nbytes, st)
 
 
 class PreparedCall:

@@ -86,6 +86,9 @@ enum {
  * SPARSE row needs them to match with discoveries >= discoveries_required.
  * A DISCOVER_UNION row whose window is broken runs dense and sets
  * discoveries = 0, so the rest of that token runs dense too.
+ * reserved: a per-call arrival count of the library; it must be 0 whenever
+ * no call is in flight (zero-initialise the tags), and every call leaves it
+ * at 0.
  */
 typedef struct wise_tag {
   int64_t request;
@@ -183,8 +186,10 @@ wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
 /* Merge the splits of the preceding decode call into a->out; for discovery
  * rows run the eta selection, write/OR the support, update the tags and
  * the counters.  `a` and `s` must describe the same call as the decode
- * call.  After wise_decode_dense, s may be NULL; if given, only its
- * counters are touched (data errors), never the support or the tags. */
+ * call (s == NULL after wise_decode_dense).  When every unit's work items
+ * fit one split workgroup (ceil(ceil(max_ctx/32)/8) <= 4, i.e. max_ctx <=
+ * 1024, and heads <= 255) the decode call has already done all of this in
+ * the same kernel, and this call only validates its arguments. */
 wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws,
                                size_t ws_bytes, void *stream);
 
@@ -228,16 +233,17 @@ wise_status wise_discover_lse(const wise_attn *a, const wise_support *s,
  * Every head of a row then attends the same tokens: run any paged dense
  * decode over (bt_out, ctx_out), e.g. wise_decode_dense with a copy of `a`
  * whose block_table, bt_stride and ctx_len are bt_out, bt_out_stride and
- * ctx_out, followed by wise_finish_select(copy, s) (a dense call touches no
- * support state; given s, its finish counts data errors).
+ * ctx_out, followed by wise_finish_select(copy, NULL).
  *   bt_out   [rows, bt_out_stride] int32 device array, bt_out_stride >=
  *            ceil(max_ctx / page_size); entries past a row's compacted
  *            pages are left untouched.  Must not be a->block_table.
  *   ctx_out  [rows] int32 device array; must not be a->ctx_len.
- * Data errors are left for the attention call to flag: a context outside
- * [1, max_ctx] is copied as is; another row mode, a slot out of range or an
- * empty head union give ctx_out = 0.  `a` describes the attention call (q,
- * k_cache, block_table, ctx_len, sizes); v_cache and out are not read.
+ * Data errors -- another row mode, a context outside [1, max_ctx], a slot
+ * out of range, an empty head union, a kept page id outside
+ * [0, num_pages) -- give ctx_out = 0 (the attention call then writes NaN
+ * for the row) and add heads to counters[WISE_CTR_ERRORS].  `a` describes
+ * the attention call (q, k_cache, block_table, ctx_len, num_pages, sizes);
+ * v_cache and out are not read.
  * Enqueues one kernel; no workspace.
  */
 wise_status wise_compact_pages(const wise_attn *a, const wise_support *s,

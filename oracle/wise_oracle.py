@@ -518,8 +518,9 @@ def run_page_union_call(*, q, k_cache, v_cache, block_table, ctx_len, page_size:
     context is the number of tokens they hold, so every kept page but the
     last is full.  Every head of a row attends the same tokens, renormalised
     within them.  Data errors (context outside [1, max_ctx], another mode, a
-    slot out of range, an empty union, a kept page id out of range) give NaN
-    for every head of the row and count one error per head.
+    slot out of range, an empty union, a kept page id out of range) give a
+    compacted context of 0, NaN for every head of the row and one error per
+    head.
     """
     R, H, d = q.shape
     P = page_size
@@ -536,7 +537,6 @@ def run_page_union_call(*, q, k_cache, v_cache, block_table, ctx_len, page_size:
             counters[3] += H
             continue
         if not 1 <= n <= max_ctx:
-            ctx_out[r] = n
             counters[3] += H
             continue
         npg = (n + P - 1) // P
@@ -556,12 +556,12 @@ def run_page_union_call(*, q, k_cache, v_cache, block_table, ctx_len, page_size:
                     continue
                 pages = union_pages(blocks, n, P)
         phys = np.asarray(block_table[r])[pages]
-        kept[r] = pages
-        tables[r] = phys
-        ctx_out[r] = len(page_tokens(pages, n, P))
         if np.any((phys < 0) | (phys >= num_pages)):
             counters[3] += H
             continue
+        kept[r] = pages
+        tables[r] = phys
+        ctx_out[r] = len(page_tokens(pages, n, P))
         toks = page_tokens(pages, n, P)
         qf = widen(q[r])
         for h in range(H):

@@ -232,10 +232,10 @@ def check_page_union(w: synth.Workload, li: synth.LayerInputs, dev: harness.Devi
                      required: Optional[int] = None, row_modes: Optional[np.ndarray] = None,
                      rows: Optional[Sequence[int]] = None) -> Report:
     """One reuse depth by the head-union page route on the GPU (compaction,
-    then the dense decode over the compacted table, whose finish counts data
-    errors) against ``O.run_page_union_call``: compacted tables and contexts
-    exact, outputs within tolerance, fallback and error counts exact, the
-    support state untouched."""
+    which counts fallbacks and data errors, then the dense decode over the
+    compacted table) against ``O.run_page_union_call``: compacted tables and
+    contexts exact, outputs within tolerance, fallback and error counts
+    exact, the support state untouched."""
     import torch
     R, H = li.q.shape[:2]
     required = w.discoveries if required is None else required
@@ -249,7 +249,7 @@ def check_page_union(w: synth.Workload, li: synth.LayerInputs, dev: harness.Devi
         rm_dev = torch.from_numpy(row_modes.astype(np.uint8)).to(dev.q.device)
     pu = harness.PageUnion(dev)
     pu.compact(state, layer_idx=layer, required=required, row_mode=rm_dev)
-    pu.attend(ws, state, layer_idx=layer)
+    pu.attend(ws)
     torch.cuda.synchronize()
     slot_of_row = None if state.slot_of_row is None else state.slot_of_row.cpu().numpy()
     ref = O.run_page_union_call(q=li.q, k_cache=li.k, v_cache=li.v, block_table=li.block_table,

@@ -118,7 +118,7 @@ def test_page_union_all_blocks_is_dense_bitwise(torch):
     pu = harness.PageUnion(dev)
     pu.compact(state, required=2)
     dev.out.fill_(float("nan"))
-    pu.attend(ws, state)
+    pu.attend(ws)
     torch.cuda.synchronize()
     assert torch.equal(pu.ctx, dev.ctx_len)
     assert torch.equal(pu.bt, dev.block_table)

@@ -546,7 +546,7 @@ def test_page_union_call():
     assert ok.counters[3] == 0 and not np.isnan(ok.out).any()
     bad["block_table"][0, 8] = -2
     hit = O.run_page_union_call(**bad, support=part, tags=tags, **common)
-    assert hit.counters[3] == 2 and np.isnan(hit.out).all()
+    assert hit.counters[3] == 2 and np.isnan(hit.out).all() and hit.ctx[0] == 0
     # one selected block inside a 256-token page keeps the whole page
     case2, _, _ = paged_case(rng, 600, H=1, P=256)
     one = np.zeros((1, 1, 1, 1), np.uint32)
