@@ -30,7 +30,8 @@ def split_source_digest() -> str:
 
 
 def short(name: str) -> str:
-    for key in ("split_static_kernel", "split_listed_kernel", "plan_kernel", "finish_kernel"):
+    for key in ("split_fused_kernel", "split_static_kernel", "split_listed_kernel", "plan_kernel", "finish_kernel",
+                "compact_pages_kernel", "snapshot_kernel", "restore_kernel"):
         if key in name:
             tmpl = name[name.find("<"): name.find(">") + 1] if "<" in name else ""
             return key + tmpl
