@@ -117,7 +117,7 @@ def cpu_baseline(w, min_s=10.0, max_rows=32):
                 res = O.run_call(q=li.q, k_cache=li.k, v_cache=li.v, block_table=li.block_table,
                                  ctx_len=li.ctx_len, page_size=w.page_size, num_pages=li.num_pages,
                                  max_ctx=w.max_ctx, modes=[mode] * R, support=sup, tags=tags,
-                                 row_request=req, row_position=pos, required=w.discoveries,
+                                 row_request=req, row_position=pos, required=max(1, w.discoveries),
                                  eta=w.eta, rows=sample_rows)
                 t_total += time.perf_counter() - t0
                 sup, tags = res.support, res.tags
@@ -159,7 +159,7 @@ class Plan:
         import torch
         self.w = w
         self.ctx = synth.context_lengths(w)
-        self.mixed = w.name == "ctx8k_mixed"
+        self.mixed = w.mix is not None
         # distinct KV sets: replicas x depths x (layer groups)
         self.kv_layers = min(w.layers, args.kv_layers)
         self.replicas = args.replicas
@@ -189,24 +189,36 @@ class Plan:
             lst = []
             if self.mixed:
                 pc = harness.PreparedCall(self.kv[(rep, 2, 0)], self.ws, W.WISE_SPARSE, self.state,
-                                          required=w.discoveries, eta=w.eta, row_mode=self.mixed_modes)
+                                          required=max(1, w.discoveries), eta=w.eta, row_mode=self.mixed_modes)
                 lst.append((pc, ("mixed", 2, 0)))
             else:
                 for depth, mode in enumerate(w.schedule):
                     for layer in range(w.layers):
                         pc = harness.PreparedCall(self.kv[(rep, depth, layer % self.kv_layers)], self.ws, mode,
-                                                  self.state, layer_idx=layer, required=w.discoveries, eta=w.eta)
+                                                  self.state, layer_idx=layer, required=max(1, w.discoveries), eta=w.eta)
                         lst.append((pc, (MODE_NAME[mode], depth, layer)))
             self.calls[rep] = lst
         self.calls_per_step = len(self.calls[0])
 
     def setup(self, rep, stream):
-        """Untimed depths that precede the mixed launch (discovery of its rows)."""
+        """Untimed work that precedes a step: the discovery depths of the
+        mixed launch's rows, or the fixed random support of a kernel-bench
+        workload (with tags that admit reuse)."""
+        if self.w.fixed_density is not None:
+            import torch
+            w, st = self.w, self.state
+            for layer in range(w.layers):
+                bits = synth.random_support(w, w.fixed_density, self.ctx, st.words, layer=layer)
+                st.support[:, layer] = torch.from_numpy(bits.view(np.int32)).to(st.support.device)
+            st.tags[:, :, 0] = st.row_request[:, None]
+            st.tags[:, :, 1] = st.row_position[:, None]
+            st.tags[:, :, 2] = max(1, w.discoveries)
+            return
         if not self.mixed:
             return
         for depth in (0, 1):
             harness.PreparedCall(self.kv[(rep, depth, 0)], self.ws, W.WISE_SPARSE, self.state,
-                                 required=self.w.discoveries, eta=self.w.eta,
+                                 required=max(1, self.w.discoveries), eta=self.w.eta,
                                  row_mode=self.setup_modes[depth]).run(stream)
 
     def eff_modes(self, key):
@@ -416,14 +428,14 @@ def main():
             pus = [(harness.PageUnion(plan.kv[(0, depth, layer % plan.kv_layers)]), layer)
                    for _, depth, layer in sparse_keys]
             for pu, layer in pus:
-                pu.compact(plan.state, layer, w.discoveries, stream=sh)
+                pu.compact(plan.state, layer, max(1, w.discoveries), stream=sh)
                 pu.attend(plan.ws, stream=sh)
             n_it = max(20, 2 * len(pus))
             ev4 = harness.HipEvents(4 * n_it + 2)
             L = W.lib()
             prepared = []                    # ctypes arguments built once: issuing stays ahead of the GPU
             for pu, layer in pus:
-                a_c, s_c, a_d = pu.layer.attn(), plan.state.view(layer, w.discoveries, w.eta), pu.attend_attn()
+                a_c, s_c, a_d = pu.layer.attn(), plan.state.view(layer, max(1, w.discoveries), w.eta), pu.attend_attn()
                 prepared.append((a_c, s_c, a_d, int(pu.bt.data_ptr()), pu.bt.stride(0), int(pu.ctx.data_ptr())))
             ev4.record(4 * n_it, sh)
             for it in range(n_it):           # back to back

@@ -93,6 +93,13 @@ class Workload:
     eta: float = 0.95
     spare_pages: int = 3
     shared_hot: bool = False        # one set of planted blocks per (row, layer), shared by the heads
+    # one-launch mixed batch: fractions of (dense, discover, sparse) rows and
+    # the fraction of sparse rows left with an incomplete discovery
+    mix: Optional[Tuple[float, float, float]] = None
+    mix_flagged: float = 0.0
+    # reuse depths read a random support of this density set directly
+    # (no discovery), as a kernel benchmark does
+    fixed_density: Optional[float] = None
     note: str = ""
 
     @property
@@ -125,7 +132,7 @@ WORKLOADS: Dict[str, Workload] = {
         note="64 rows at 4K, 24 layers looped per depth"),
     "ctx8k_mixed": Workload(
         name="ctx8k_mixed", rows=64, heads=16, head_dim=128, dtype="bf16", page_size=16,
-        shuffle=True, alpha=2.5, seed=3, ctx=8192, hot=4,
+        shuffle=True, alpha=2.5, seed=3, ctx=8192, hot=4, mix=(0.25, 0.25, 0.5), mix_flagged=0.05,
         note="64 rows at 8K; one launch mixes dense/discover/sparse rows"),
     "ragged": Workload(
         name="ragged", rows=128, heads=16, head_dim=128, dtype="bf16", page_size=16,
@@ -144,6 +151,17 @@ WORKLOADS: Dict[str, Workload] = {
         name="match8k", rows=64, heads=16, head_dim=128, dtype="bf16", page_size=16,
         shuffle=True, alpha=8.0, seed=13, ctx=8192, hot=38,
         note="supplementary: ~0.15 union density at 8K"),
+    # supplementary analogs of the pull request's kernel benchmark ("Results"):
+    # 1K x 64 with the support set directly to a random 0.13 of the blocks,
+    # and a 4K x 20 launch of half discovery and half sparse rows
+    "kbench1k": Workload(
+        name="kbench1k", rows=64, heads=16, head_dim=128, dtype="bf16", page_size=16,
+        shuffle=True, alpha=2.5, seed=15, ctx=1024, hot=4, schedule=(SPARSE,), fixed_density=0.13,
+        note="supplementary: kernel benchmark, 1K x 64, random support density 0.13"),
+    "mix4k": Workload(
+        name="mix4k", rows=20, heads=16, head_dim=128, dtype="bf16", page_size=16,
+        shuffle=True, alpha=8.0, seed=16, ctx=4096, hot=23, mix=(0.0, 0.5, 0.5),
+        note="supplementary: kernel benchmark, 4K x 20, half discovery and half sparse rows"),
     # supplementary, for the head-union page-granular route: the heads of a row
     # share their planted blocks (heads attending the same positions)
     "shared8k": Workload(
@@ -347,17 +365,19 @@ def layer_inputs(w: Workload, depth: int, layer: int = 0,
 
 
 def mixed_row_modes(w: Workload, discover_union_alt: bool = True) -> Tuple[np.ndarray, np.ndarray]:
-    """Row modes of the one-launch mixed batch: 25% dense, 25% discover, 50% sparse.
+    """Row modes of the one-launch mixed batch: fractions ``w.mix`` of dense,
+    discover and sparse rows (25% / 25% / 50% for the 8K mixed batch).
 
-    Discover rows alternate DISCOVER / DISCOVER_UNION.  5% of the sparse rows
-    (rounded, at least one) are returned as ``flagged``: their discovery is
-    to be left incomplete, so they must fall back to dense.
+    Discover rows alternate DISCOVER / DISCOVER_UNION.  A fraction
+    ``w.mix_flagged`` of the sparse rows (rounded, at least one when it is
+    positive) are returned as ``flagged``: their discovery is to be left
+    incomplete, so they must fall back to dense.
     Returns (modes uint8 [rows], flagged bool [rows]).
     """
     R = w.rows
     g = _rng(w.seed, _S_MODES)
     perm = g.permutation(R)
-    nd, nc = R // 4, R // 4
+    nd, nc = int(R * w.mix[0]), int(R * w.mix[1])
     modes = np.empty(R, dtype=np.uint8)
     modes[perm[:nd]] = DENSE
     disc = perm[nd: nd + nc]
@@ -365,9 +385,10 @@ def mixed_row_modes(w: Workload, discover_union_alt: bool = True) -> Tuple[np.nd
         modes[r] = DISCOVER_UNION if (discover_union_alt and i % 2) else DISCOVER
     sparse = perm[nd + nc:]
     modes[sparse] = SPARSE
-    nflag = max(1, int(round(0.05 * len(sparse))))
     flagged = np.zeros(R, dtype=bool)
-    flagged[np.sort(g.choice(sparse, size=nflag, replace=False))] = True
+    if w.mix_flagged > 0:
+        nflag = max(1, int(round(w.mix_flagged * len(sparse))))
+        flagged[np.sort(g.choice(sparse, size=nflag, replace=False))] = True
     return modes, flagged
 
 
