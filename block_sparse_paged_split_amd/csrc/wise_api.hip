@@ -9,9 +9,16 @@
 
 namespace wise {
 
-int tiles_per_item(int max_blocks) {
-  (void)max_blocks;
-  return 8;  // ~eight tiles per program, as the split design prescribes
+int tiles_per_item(int max_blocks, int64_t units) {
+  // About eight tiles per program, as the split design prescribes.  A launch
+  // with few items (a small batch of short rows) cuts them shorter, so that
+  // more waves run at once, while a unit stays within one fused workgroup of
+  // at most kMaxFusedItems items.
+  const int64_t items8 = units * ((max_blocks + 7) / 8);
+  if (items8 >= kSmallLaunchItems || max_blocks > kMaxFusedBlocks) return 8;
+  int t = 1;
+  while (t < 8 && (max_blocks + t - 1) / t > kMaxFusedItems) t <<= 1;
+  return t;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -26,7 +33,7 @@ bool make_layout(int rows, int heads, int head_dim, int max_ctx, Layout *L) {
   L->head_dim = head_dim;
   L->max_ctx = max_ctx;
   L->max_blocks = (max_ctx + kBlock - 1) / kBlock;
-  L->tiles_per_item = tiles_per_item(L->max_blocks);
+  L->tiles_per_item = tiles_per_item(L->max_blocks, static_cast<int64_t>(rows) * heads);
   L->items_per_unit = (L->max_blocks + L->tiles_per_item - 1) / L->tiles_per_item;
   if (L->items_per_unit > kMaxItemsPerUnit || L->tiles_per_item > kMaxTilesPerItem) return false;
   const size_t units = static_cast<size_t>(rows) * heads;
@@ -203,10 +210,10 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
   // spans several split workgroups, plan first and run the persistent split
   // over the compact item list; otherwise the static grid has one workgroup
   // per unit and no empty slots worth removing.
-  const bool listed = (row_mode != nullptr || uniform_mode == WISE_SPARSE) && p.chunk_groups > 1;
   // units that fit one split workgroup are also finished by it (the paired
   // wise_finish_select then has nothing left to do)
-  const bool fused = !k_only && fused_finish_shape(L, a->heads);
+  const bool fused = !k_only && fused_finish_shape(L, a->heads, a->dtype);
+  const bool listed = !fused && (row_mode != nullptr || uniform_mode == WISE_SPARSE) && p.chunk_groups > 1;
   const int cus = listed ? compute_units() : 0;
   if (listed && cus <= 0) return WISE_E_HIP;
   if (launch_split(p, a->dtype, a->head_dim, listed, k_only, fused, cus,
@@ -228,7 +235,7 @@ wise_status finish(const wise_attn *a, const wise_support *s, const float *lse, 
   st = check_ws(ws, ws_bytes, L);
   if (st != WISE_OK) return st;
   // the decode call already finished these units (see decode())
-  if (lse == nullptr && fused_finish_shape(L, a->heads)) return WISE_OK;
+  if (lse == nullptr && fused_finish_shape(L, a->heads, a->dtype)) return WISE_OK;
   char *w = static_cast<char *>(ws);
   FinishParams p{};
   p.rows = a->rows;

@@ -28,7 +28,10 @@ __host__ __device__ inline int encode_row(int eff, int req) { return (eff & 0xF)
 // Work decomposition: unit = (row, head); a unit's attended tiles (all causal
 // tiles, or the support's tiles in ascending order) are cut into work items of
 // tiles_per_item consecutive list entries.  One wave per item slot.
-int tiles_per_item(int max_blocks);
+int tiles_per_item(int max_blocks, int64_t units);
+constexpr int64_t kSmallLaunchItems = 1024;  // below this many 8-tile items a launch cuts items shorter
+constexpr int kMaxFusedItems = 16;            // items (waves) of one fused split + finish workgroup
+constexpr int kMaxFusedBlocks = 64;           // blocks of a fused unit (one per lane in its selection)
 
 struct Layout {
   int rows, heads, head_dim, max_ctx, max_blocks, tiles_per_item, items_per_unit;
@@ -141,11 +144,18 @@ hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool list
                         int cus, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 
 // The finish is fused into the split kernel when every unit's items fit one
-// split workgroup (one wave per item) and a row's heads fit the 8-bit
-// arrival count kept in the tag's reserved word.  Decode and finish calls
-// take the same decision from the same sizes.
-inline bool fused_finish_shape(const Layout &L, int heads) {
-  return L.items_per_unit <= kWavesPerGroup && heads <= 255;
+// split workgroup (one wave per item): up to 4 items at eight tiles each, or
+// up to 16 (8 for fp32 at head_dim 128, whose waves need more than 128
+// registers) when a small launch cut its items shorter; a unit has at most 64
+// blocks, and a row's heads fit the 8-bit arrival count kept in the tag's
+// reserved word.  Decode and finish calls take the same decision from the
+// same sizes.
+inline int fused_max_items(const Layout &L, int dtype) {
+  if (L.tiles_per_item >= 8) return kWavesPerGroup;
+  return (dtype == WISE_F32 && L.head_dim == 128) ? 8 : kMaxFusedItems;
+}
+inline bool fused_finish_shape(const Layout &L, int heads, int dtype) {
+  return L.items_per_unit <= fused_max_items(L, dtype) && L.max_blocks <= kMaxFusedBlocks && heads <= 255;
 }
 hipError_t launch_finish(const FinishParams &p, hipStream_t stream);
 hipError_t launch_compact_pages(const PageParams &p, hipStream_t stream);

@@ -514,13 +514,14 @@ __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan
   }
 }
 
-template <bool kBf16, int D>
-__global__ __launch_bounds__(64 * kWavesPerGroup) void split_fused_kernel(const SplitParams p) {
-  __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
-  __shared__ float s_acc[kWavesPerGroup * D];
-  __shared__ float2 s_ml[kWavesPerGroup];
-  __shared__ float2 s_st[kWavesPerGroup * kMaxTilesPerItem];
-  __shared__ float s_w[kWavesPerGroup];
+template <bool kBf16, int D, int W>
+__global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p) {
+  static_assert(W * kMaxTilesPerItem >= kMaxFusedBlocks, "tile stats of a fused unit must fit");
+  __shared__ int s_tiles[W][kMaxTilesPerItem];
+  __shared__ float s_acc[W * D];
+  __shared__ float2 s_ml[W];
+  __shared__ float2 s_st[W * kMaxTilesPerItem];
+  __shared__ float s_w[W];
   __shared__ uint32_t s_bits[kMaxWords];
   const int lane = threadIdx.x & 63;
   const int k = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);  // item slot
@@ -666,10 +667,18 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, b
   } else {
     const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
     if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipErrorInvalidValue;
-    if (fused)
-      hipLaunchKernelGGL((split_fused_kernel<kBf16, D>), dim3(static_cast<unsigned>(p.rows) * p.heads), block, 0,
-                         stream, p);
-    else if (k_only)
+    if (fused) {
+      // one workgroup per unit, one wave per item slot
+      const dim3 units(static_cast<unsigned>(p.rows) * p.heads);
+      if (p.items_per_unit <= 4)
+        hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 4>), units, dim3(64 * 4), 0, stream, p);
+      else if (p.items_per_unit <= 8)
+        hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 8>), units, dim3(64 * 8), 0, stream, p);
+      else if constexpr (kBf16 || D == 64)
+        hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 16>), units, dim3(64 * 16), 0, stream, p);
+      else
+        return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
+    } else if (k_only)
       hipLaunchKernelGGL((split_static_kernel<kBf16, D, true>), grid, block, 0, stream, p);
     else
       hipLaunchKernelGGL((split_static_kernel<kBf16, D, false>), grid, block, 0, stream, p);
@@ -683,7 +692,8 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, b
 hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, bool fused,
                         int cus, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
   if (listed && (k_only || fused)) return hipErrorInvalidValue;  // K-only and fused calls use the static grid
-  if (fused && (k_only || p.chunk_groups != 1)) return hipErrorInvalidValue;
+  if (fused && (k_only || p.items_per_unit > kMaxFusedItems || p.max_blocks > kMaxFusedBlocks))
+    return hipErrorInvalidValue;
   if (dtype == WISE_BF16 && head_dim == 128)
     return launch_typed<true, 128>(p, listed, k_only, fused, cus, ev_begin, ev_end, stream);
   if (dtype == WISE_BF16 && head_dim == 64)

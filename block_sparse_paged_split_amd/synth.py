@@ -162,6 +162,11 @@ WORKLOADS: Dict[str, Workload] = {
         name="mix4k", rows=20, heads=16, head_dim=128, dtype="bf16", page_size=16,
         shuffle=True, alpha=8.0, seed=16, ctx=4096, hot=23, mix=(0.0, 0.5, 0.5),
         note="supplementary: kernel benchmark, 4K x 20, half discovery and half sparse rows"),
+    # supplementary: a small batch (two rows), latency-bound
+    "small1k": Workload(
+        name="small1k", rows=2, heads=16, head_dim=128, dtype="bf16", page_size=16,
+        shuffle=True, alpha=2.5, seed=17, ctx=1024, hot=4,
+        note="supplementary: 2 rows at 1K, a latency-bound small batch"),
     # supplementary, for the head-union page-granular route: the heads of a row
     # share their planted blocks (heads attending the same positions)
     "shared8k": Workload(

@@ -154,6 +154,17 @@ def test_ragged_contexts(torch, dtype, d, P):
     run_schedule(w)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("ctxs", [(1, 31, 33, 100, 257, 1000, 2048), (5, 40, 256)])
+def test_small_launches(torch, dtype, d, ctxs):
+    """Launches with few work items cut them to 1-4 tiles, and units of up
+    to 16 items finish inside the split kernel (8 for fp32 at d 128)."""
+    w = synth.Workload(name=f"small_{dtype}{d}_{len(ctxs)}", rows=len(ctxs), heads=3, head_dim=d,
+                       dtype=dtype, page_size=16, shuffle=True, alpha=6.0, seed=71, ctx_list=ctxs, hot=2,
+                       schedule=(1, 2, 3), eta=0.9)
+    run_schedule(w)
+
+
 def test_page_size_and_layout_invariance(torch):
     """Physical layout changes nothing: same bits for page sizes 8..64, a
     shuffled or identity block table, and [pages, P, H, d] storage."""
