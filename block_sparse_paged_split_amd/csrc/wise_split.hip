@@ -217,10 +217,9 @@ struct UnitLds {
 
 template <bool kBf16, int D, bool kKOnly>
 __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int h, int k, int n, bool sparse,
-                                         int count, uint32_t word, int incl, int lane, int *tiles,
+                                         int count, uint32_t word, int incl, int lane, int *tiles, int T,
                                          const UnitLds *lds = nullptr) {
   using G = Geo<kBf16, D>;
-  const int T = p.tiles_per_item;
   const int first = k * T;
   const int ntiles = min(T, count - first);
 
@@ -422,7 +421,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
     }
   }
   if (k >= items) return;
-  run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave]);
+  run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave],
+                             p.tiles_per_item);
 }
 
 // ---------------------------------------------------------------------------
@@ -534,12 +534,15 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   uint32_t word = 0u;
   int incl = 0;
   const int count = sparse ? support_scan(p, rp.slot, h, nb, lane, word, incl) : nb;
-  const int items = (count + p.tiles_per_item - 1) / p.tiles_per_item;
+  // the unit's list entries spread evenly over the workgroup's waves (the
+  // partials stay in LDS, so the item size need not match the workspace's)
+  const int T = max(1, (count + W - 1) / W);
+  const int items = (count + T - 1) / T;
   if (k == 0 && lane == 0 && h == 0 && rp.fallback && p.counters)
     atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
   const UnitLds lds{s_acc, s_ml, s_st};
   if (k < items)
-    run_item<kBf16, D, false>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], &lds);
+    run_item<kBf16, D, false>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], T, &lds);
   __syncthreads();  // every wave of the workgroup reaches this once
   if (k == 0) finish_fused<D>(p, rp, u, h, nb, items, s_acc, s_ml, s_st, s_w, s_bits, lane);
 }
@@ -627,7 +630,7 @@ void split_listed_kernel(const SplitParams p) {
     int incl = 0;
     const int nb = (n + kBlock - 1) / kBlock;
     const int count = sparse ? support_scan(p, slot, h, nb, lane, word, incl) : nb;
-    run_item<kBf16, D, false>(p, u, r, h, k, n, sparse, count, word, incl, lane, s_tiles[wave]);
+    run_item<kBf16, D, false>(p, u, r, h, k, n, sparse, count, word, incl, lane, s_tiles[wave], p.tiles_per_item);
   }
 }
 
