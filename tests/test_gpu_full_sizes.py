@@ -113,3 +113,30 @@ def test_ragged_eta_sweep(torch):
         say(f"   eta {eta}: union density {ctr[W.CTR_SELECTED] / ctr[W.CTR_CAUSAL]:.4f}")
     a, b, c = first_depth[0.9], first_depth[0.95], first_depth[0.99]
     assert ((a & ~b) == 0).all() and ((b & ~c) == 0).all()
+
+
+def test_lse_route_ragged_full_size(torch):
+    """Discovery and union by the LSE route on the 128-row ragged batch
+    (contexts 512..32768): every row runs on the GPU, sampled rows (the
+    shortest, the longest, the median and two others) are checked against
+    the oracle; the LSE of the other rows is the same oracle's where sampled
+    and 0 elsewhere (those rows are not checked)."""
+    from parity import check_lse_call, oracle_lse
+    w = synth.WORKLOADS["ragged"]
+    ctx = synth.context_lengths(w)
+    order = np.argsort(ctx)
+    rows = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 5, 77})
+    say(f"[ragged lse] checked rows {rows} contexts {[int(ctx[r]) for r in rows]}")
+    state = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    for depth, union in ((0, False), (1, True)):
+        li = synth.layer_inputs(w, depth)
+        dev = harness.upload(li, with_stats=True)
+        del li
+        sample = synth.layer_inputs(w, depth, rows=rows)
+        say(f"   depth {depth} union {union}")
+        rep = check_lse_call(w, sample, dev, ws, state, oracle_lse(w, sample, rows), union=union, rows=rows)
+        say(f"   near_eta {rep.near_eta} near_tie {rep.near_tie} mismatch {rep.support_mismatch}")
+        del dev
+    disc = state.tags_numpy()["discoveries"][:, 0]
+    assert (disc[rows] == 2).all()
