@@ -144,7 +144,8 @@ int log2i(int x) {
 }
 
 wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, const uint8_t *row_mode,
-                   void *ws, size_t ws_bytes, void *stream, bool k_only = false) {
+                   void *ws, size_t ws_bytes, void *stream, const float *lse = nullptr) {
+  const bool k_only = lse != nullptr;  // the LSE route reads K only
   Layout L;
   wise_status st = check_attn(a, &L, k_only);
   if (st != WISE_OK) return st;
@@ -212,7 +213,8 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
   // per unit and no empty slots worth removing.
   // units that fit one split workgroup are also finished by it (the paired
   // wise_finish_select then has nothing left to do)
-  const bool fused = !k_only && fused_finish_shape(L, a->heads, a->dtype);
+  const bool fused = fused_finish_shape(L, a->heads, a->dtype);
+  p.lse = lse;
   const bool listed = !fused && (row_mode != nullptr || uniform_mode == WISE_SPARSE) && p.chunk_groups > 1;
   const int cus = listed ? compute_units() : 0;
   if (listed && cus <= 0) return WISE_E_HIP;
@@ -235,7 +237,7 @@ wise_status finish(const wise_attn *a, const wise_support *s, const float *lse, 
   st = check_ws(ws, ws_bytes, L);
   if (st != WISE_OK) return st;
   // the decode call already finished these units (see decode())
-  if (lse == nullptr && fused_finish_shape(L, a->heads, a->dtype)) return WISE_OK;
+  if (fused_finish_shape(L, a->heads, a->dtype)) return WISE_OK;
   char *w = static_cast<char *>(ws);
   FinishParams p{};
   p.rows = a->rows;
@@ -308,7 +310,7 @@ wise_status wise_discover_lse(const wise_attn *a, const wise_support *s, int32_t
   if (st == WISE_OK) st = check_ws(ws, ws_bytes, L);
   if (st != WISE_OK) return st;
   st = decode(a, s, union_with_previous ? WISE_DISCOVER_UNION : WISE_DISCOVER, nullptr, ws, ws_bytes, stream,
-              true);
+              lse);
   if (st != WISE_OK) return st;
   return finish(a, s, lse, ws, ws_bytes, stream);
 }

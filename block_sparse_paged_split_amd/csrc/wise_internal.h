@@ -61,9 +61,11 @@ struct SplitParams {
   wise_tag *tags;
   const int64_t *row_request, *row_position;
   unsigned long long *counters;
-  // fused split + finish only: the output and the selection target
+  // fused split + finish only: the output, the selection target, and the
+  // external LSE of the LSE route ([rows * heads], natural log)
   float *out;
   float eta;
+  const float *lse;
   // workspace and optional export
   int32_t *row_code, *unit_items;
   unsigned long long *row_done;

@@ -437,30 +437,48 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
 // unit of the row planned from the tag before any head arrives, so the
 // update cannot race with a plan.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool kKOnly>
 __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan &rp, int u, int h, int nb,
                                              int items, const float *s_acc, const float2 *s_ml,
                                              const float2 *s_st, float *s_w, uint32_t *s_bits, int lane) {
   const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
   const bool discover = stateful && (rp.eff == WISE_DISCOVER || rp.eff == WISE_DISCOVER_UNION);
-  // merge: M = max m_i, w_i = 2^(m_i - M), L = sum l_i w_i, out = sum acc_i w_i / L
-  const float2 ml = lane < items ? s_ml[lane] : make_float2(-INFINITY, 0.0f);
-  const float M = sel::wave_max(ml.x);
-  const bool err = items == 0 || __builtin_amdgcn_ballot_w64(ml.y < 0.0f) != 0ull;
-  float Lp = 0.0f;
-  if (lane < items) {
-    const float w = __builtin_amdgcn_exp2f(ml.x - M);
-    s_w[lane] = w;
-    Lp = fmaf(ml.y, w, Lp);
+  if constexpr (kKOnly) {
+    // LSE route: a row whose union window broke did no work; its tag is invalidated
+    if (!discover && !rp.bad) {
+      if (stateful && rp.req == WISE_DISCOVER_UNION && h == 0 && lane == 0)
+        p.tags[static_cast<int64_t>(rp.slot) * p.layers + p.layer].discoveries = 0;
+      return;
+    }
   }
-  const float L = sel::wave_sum(Lp);
+  const float2 ml = lane < items ? s_ml[lane] : make_float2(-INFINITY, 0.0f);
+  float M = sel::wave_max(ml.x);
+  bool err = items == 0 || __builtin_amdgcn_ballot_w64(ml.y < 0.0f) != 0ull;
+  float L = 1.0f;
+  if constexpr (kKOnly) {
+    // masses relative to the external kernel's normaliser: M = lse in base-2 units, L = 1
+    const float lse = p.lse[u];
+    err = err || !__builtin_isfinite(lse);
+    M = lse * 1.44269504088896340736f;
+  } else {
+    // merge: M = max m_i, w_i = 2^(m_i - M), L = sum l_i w_i, out = sum acc_i w_i / L
+    float Lp = 0.0f;
+    if (lane < items) {
+      const float w = __builtin_amdgcn_exp2f(ml.x - M);
+      s_w[lane] = w;
+      Lp = fmaf(ml.y, w, Lp);
+    }
+    L = sel::wave_sum(Lp);
+  }
   if (discover)
     for (int w = lane; w < kMaxWords; w += 64) s_bits[w] = 0u;
   sel::wave_lds_sync();
-  for (int dd = lane; dd < D; dd += 64) {
-    float a = 0.0f;
-    for (int t = 0; t < items; ++t) a = fmaf(s_acc[t * D + dd], s_w[t], a);
-    p.out[static_cast<int64_t>(u) * D + dd] = err ? __builtin_nanf("") : a / L;
+  if constexpr (!kKOnly) {
+    for (int dd = lane; dd < D; dd += 64) {
+      float a = 0.0f;
+      for (int t = 0; t < items; ++t) a = fmaf(s_acc[t * D + dd], s_w[t], a);
+      p.out[static_cast<int64_t>(u) * D + dd] = err ? __builtin_nanf("") : a / L;
+    }
   }
   if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
   if (!stateful) return;
@@ -514,7 +532,7 @@ __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan
   }
 }
 
-template <bool kBf16, int D, int W>
+template <bool kBf16, int D, int W, bool kKOnly>
 __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p) {
   static_assert(W * kMaxTilesPerItem >= kMaxFusedBlocks, "tile stats of a fused unit must fit");
   __shared__ int s_tiles[W][kMaxTilesPerItem];
@@ -533,7 +551,10 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   const bool sparse = !rp.bad && rp.eff == WISE_SPARSE;
   uint32_t word = 0u;
   int incl = 0;
-  const int count = sparse ? support_scan(p, rp.slot, h, nb, lane, word, incl) : nb;
+  // K-only calls have nothing to do for a row whose discovery window broke
+  const int count = (kKOnly && rp.eff == WISE_DENSE) ? 0
+                    : sparse                         ? support_scan(p, rp.slot, h, nb, lane, word, incl)
+                                                     : nb;
   // the unit's list entries spread evenly over the workgroup's waves (the
   // partials stay in LDS, so the item size need not match the workspace's)
   const int T = max(1, (count + W - 1) / W);
@@ -542,9 +563,9 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
     atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
   const UnitLds lds{s_acc, s_ml, s_st};
   if (k < items)
-    run_item<kBf16, D, false>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], T, &lds);
+    run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], T, &lds);
   __syncthreads();  // every wave of the workgroup reaches this once
-  if (k == 0) finish_fused<D>(p, rp, u, h, nb, items, s_acc, s_ml, s_st, s_w, s_bits, lane);
+  if (k == 0) finish_fused<D, kKOnly>(p, rp, u, h, nb, items, s_acc, s_ml, s_st, s_w, s_bits, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -673,14 +694,25 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, b
     if (fused) {
       // one workgroup per unit, one wave per item slot
       const dim3 units(static_cast<unsigned>(p.rows) * p.heads);
-      if (p.items_per_unit <= 4)
-        hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 4>), units, dim3(64 * 4), 0, stream, p);
-      else if (p.items_per_unit <= 8)
-        hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 8>), units, dim3(64 * 8), 0, stream, p);
-      else if constexpr (kBf16 || D == 64)
-        hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 16>), units, dim3(64 * 16), 0, stream, p);
-      else
-        return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
+      if (k_only) {
+        if (p.items_per_unit <= 4)
+          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 4, true>), units, dim3(64 * 4), 0, stream, p);
+        else if (p.items_per_unit <= 8)
+          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 8, true>), units, dim3(64 * 8), 0, stream, p);
+        else if constexpr (kBf16 || D == 64)
+          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 16, true>), units, dim3(64 * 16), 0, stream, p);
+        else
+          return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
+      } else {
+        if (p.items_per_unit <= 4)
+          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 4, false>), units, dim3(64 * 4), 0, stream, p);
+        else if (p.items_per_unit <= 8)
+          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 8, false>), units, dim3(64 * 8), 0, stream, p);
+        else if constexpr (kBf16 || D == 64)
+          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 16, false>), units, dim3(64 * 16), 0, stream, p);
+        else
+          return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
+      }
     } else if (k_only)
       hipLaunchKernelGGL((split_static_kernel<kBf16, D, true>), grid, block, 0, stream, p);
     else
@@ -695,7 +727,7 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, b
 hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, bool fused,
                         int cus, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
   if (listed && (k_only || fused)) return hipErrorInvalidValue;  // K-only and fused calls use the static grid
-  if (fused && (k_only || p.items_per_unit > kMaxFusedItems || p.max_blocks > kMaxFusedBlocks))
+  if (fused && (p.items_per_unit > kMaxFusedItems || p.max_blocks > kMaxFusedBlocks || (k_only && !p.lse)))
     return hipErrorInvalidValue;
   if (dtype == WISE_BF16 && head_dim == 128)
     return launch_typed<true, 128>(p, listed, k_only, fused, cus, ev_begin, ev_end, stream);

@@ -198,11 +198,12 @@ wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *
  * changes", second bullet: the FlashAttention route rereads K once to
  * rebuild block mass from the kernel's LSE).  Every row DISCOVER
  * (union_with_previous == 0) or DISCOVER_UNION (!= 0), with the tag rules
- * of wise_decode_discover.  One call enqueues both kernels: a split-KV pass
- * that reads q and K only and records every tile's (max, sum), then the
+ * of wise_decode_discover.  One call does both steps: a split-KV pass that
+ * reads q and K only and records every tile's (max, sum), then the
  * selection, with block mass m_b -> l_b * exp(m_b - lse) instead of the
  * merged (M, L); support, tags and counters are updated as by
- * wise_finish_select.  No attention output is written: a->v_cache and
+ * wise_finish_select (one kernel when the finish fuses into the split, see
+ * wise_finish_select; two otherwise).  No attention output is written: a->v_cache and
  * a->out are not read and may be NULL; a->tile_stats is honoured.
  *   lse  [rows, heads] fp32 device array: log(sum_t exp(scale * q.k_t))
  *        over the row's ctx_len tokens, natural log (what FlashAttention's
