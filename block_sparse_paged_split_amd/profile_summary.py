@@ -73,7 +73,7 @@ def traffic(fetch_csv: str, write_csv: str, out_md: str, workload: str, mib: int
     scale_w = known / max(cal_w[0])
     # the decode split kernel (the K-only instantiation of the LSE route is not counted)
     split = [k for k in f if "split_" in k and "kernel" in k
-             and not re.search(r"split_static_kernel<[^>]*, true>", k)]
+             and not re.search(r"split_(static|fused)_kernel<[^>]*, true>", k)]
     fk = [x for k in split for x in f[k]]
     wk = [x for k in split for x in w.get(k, [])]
     fetch_kib = sum(fk) / len(fk)
