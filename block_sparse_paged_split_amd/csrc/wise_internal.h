@@ -20,9 +20,10 @@ constexpr int kMaxItemsPerUnit = 512;  // kMaxBlocks / smallest tiles-per-item (
 constexpr int kRowError = 0xF;         // row code: bad device data for the row
 constexpr int kItemBits = 9;           // item list entry: unit << 9 | item (kMaxItemsPerUnit = 2^9)
 
-// Row code written by the split kernel (wave of head 0, item 0) and read by
-// the finish kernel: effective mode in bits 0..3 (kRowError for a bad row),
-// requested mode in bits 4..7.
+// Row code written by the static split kernel (wave of head 0, item 0) or
+// the plan kernel and read by the listed split and the finish kernels:
+// effective mode in bits 0..3 (kRowError for a bad row), requested mode in
+// bits 4..7.
 __host__ __device__ inline int encode_row(int eff, int req) { return (eff & 0xF) | ((req & 0xF) << 4); }
 
 // Work decomposition: unit = (row, head); a unit's attended tiles (all causal

@@ -10,10 +10,15 @@
 //
 // MI355X design:
 //  * One wave64 per work item (<= tiles_per_item consecutive entries of a
-//    (row, head)'s tile list); four independent waves per workgroup; the grid
-//    covers every (unit, item) slot, and each wave plans its own item (tag
-//    check, fallback, tile count, compacted tile list) so that a call is a
-//    single launch with no host readback.
+//    (row, head)'s tile list); each wave plans its own item (tag check,
+//    fallback, tile count, compacted tile list), so that a call needs no
+//    host readback.  Three launch shapes share the per-item body: the fused
+//    kernel (one workgroup per unit whose waves cover all of its items, then
+//    finish the unit in the same kernel), the static grid (four independent
+//    waves per workgroup over every (unit, item) slot, finished by the
+//    finish kernel), and the listed grid (persistent waves over the compact
+//    item list a one-workgroup plan kernel builds, for calls with sparse
+//    rows whose units span several workgroups).
 //  * A 32-token K (or V) tile is read with 16-byte loads in which each load
 //    instruction covers TPI whole tokens contiguously (1 KB per wave for
 //    bf16 d=128): lane = (token subgroup g, 16-byte dim chunk c).  Every K
@@ -376,8 +381,10 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
 
 // ---------------------------------------------------------------------------
 // Static grid: one wave per (unit, item slot); every wave plans its own item.
-// Used when no row is sparse, so every unit's item count is known from its
-// context length and (nearly) every slot holds work.
+// Used for calls the fused kernel does not cover that have no sparse rows
+// (every unit's item count then follows from its context length, so nearly
+// every slot holds work), and for sparse calls whose units fit one
+// workgroup but do not fuse.
 // ---------------------------------------------------------------------------
 template <bool kBf16, int D, bool kKOnly>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const SplitParams p) {
