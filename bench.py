@@ -129,9 +129,8 @@ def cpu_baseline(w, min_s=10.0, max_rows=32):
 
 
 def split_source_digest() -> str:
-    import hashlib
-    src = os.path.join(ROOT, "block_sparse_paged_split_amd", "csrc", "wise_split.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+    from block_sparse_paged_split_amd.profile_summary import split_source_digest as digest
+    return digest()
 
 
 def measured_traffic(workload):

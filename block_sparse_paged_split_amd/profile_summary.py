@@ -26,7 +26,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 
 def split_source_digest() -> str:
-    return hashlib.sha256(open(os.path.join(PKG, "csrc", "wise_split.hip"), "rb").read()).hexdigest()
+    """sha256 of the split kernel's source with comments and whitespace
+    removed, so that counters stay attributed across comment-only edits."""
+    text = open(os.path.join(PKG, "csrc", "wise_split.hip")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def short(name: str) -> str:
@@ -91,7 +97,8 @@ def traffic(fetch_csv: str, write_csv: str, out_md: str, workload: str, mib: int
              "dispatch summed over the L2 channels), each scaled by what the counter reads for the",
              f"calibration kernel (neg over {mib} MiB of fp32: {mib} MiB read, {mib} MiB written).",
              "bench.py reports traffic_bytes_per_launch as roofline.traffic while the split",
-             "kernel source still hashes to kernel_source_sha256.", "", "Commands:", "", "```"]
+             "kernel source, comments and whitespace removed, still hashes to",
+             "kernel_source_sha256.", "", "Commands:", "", "```"]
     lines += list(commands) + ["```", "", "```json", json.dumps(rec, indent=1), "```", ""]
     open(out_md, "w").write("\n".join(lines))
 
