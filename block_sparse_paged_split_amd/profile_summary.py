@@ -25,14 +25,20 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+# sources that decide the split kernel's code and launch shape
+DIGEST_SOURCES = ("wise_split.hip", "wise_select.h", "wise_internal.h", "wise_api.hip")
+
+
 def split_source_digest() -> str:
-    """sha256 of the split kernel's source with comments and whitespace
+    """sha256 of the split kernel's sources with comments and whitespace
     removed, so that counters stay attributed across comment-only edits."""
-    text = open(os.path.join(PKG, "csrc", "wise_split.hip")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    code = "".join(text.split())
-    return hashlib.sha256(code.encode()).hexdigest()
+    h = hashlib.sha256()
+    for name in DIGEST_SOURCES:
+        text = open(os.path.join(PKG, "csrc", name)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(name.encode() + b"\0" + "".join(text.split()).encode() + b"\0")
+    return h.hexdigest()
 
 
 def short(name: str) -> str:
@@ -97,8 +103,9 @@ def traffic(fetch_csv: str, write_csv: str, out_md: str, workload: str, mib: int
              "dispatch summed over the L2 channels), each scaled by what the counter reads for the",
              f"calibration kernel (neg over {mib} MiB of fp32: {mib} MiB read, {mib} MiB written).",
              "bench.py reports traffic_bytes_per_launch as roofline.traffic while the split",
-             "kernel source, comments and whitespace removed, still hashes to",
-             "kernel_source_sha256.", "", "Commands:", "", "```"]
+             "kernel's sources (" + ", ".join(DIGEST_SOURCES) + "),",
+             "comments and whitespace removed, still hash to kernel_source_sha256.", "",
+             "Commands:", "", "```"]
     lines += list(commands) + ["```", "", "```json", json.dumps(rec, indent=1), "```", ""]
     open(out_md, "w").write("\n".join(lines))
 
