@@ -9,8 +9,9 @@
 // first discovery depth, its selection and the causal blocks, and for a
 // union depth only the newly set blocks.
 //
-// One workgroup per row (a row with more than 16 heads takes several), one
-// wave64 per (row, head):
+// One workgroup per row for units of up to 64 blocks (a row with more than
+// 16 heads takes several), one per 4 heads for longer units; one wave64 per
+// (row, head):
 //  1. merge the unit's items: M = max m_i, w_i = 2^(m_i - M),
 //     L = sum l_i w_i, out = sum acc_i w_i / L (fixed summation orders; the
 //     loads of up to eight items are in flight together);
@@ -37,8 +38,7 @@ namespace {
 
 using namespace sel;
 
-constexpr int kUnroll = 8;
-constexpr int kHeadsPerGroup = 16;  // waves (heads) per finish workgroup
+constexpr int kHeadsPerGroup = 16;  // waves (heads) per finish workgroup of short units
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Row facts the finish of one unit needs (all from scalar loads issued together).
@@ -68,6 +68,9 @@ __device__ __forceinline__ UnitResult finish_unit(const FinishParams &p, const U
   if (lse_mode && !discover && !ui.row_bad) return UnitResult{false, 0};
 
   // ---- loads: partials, tile stats, old support words (and the LSE) ----
+  // (the partials of kUnroll items are in flight at a time; units of long
+  // rows have many items, so they keep more of them in flight)
+  constexpr int kUnroll = KPL >= 2 ? 16 : 8;
   constexpr int kDims = 2;  // head_dim <= 2 * 64
   const float *acc = p.part_acc + base * D;
   float v[kDims][kUnroll];
@@ -204,7 +207,10 @@ __device__ __forceinline__ void row_bookkeeping(const FinishParams &p, const Uni
 
 // Waves per workgroup for units of up to 64*KMAX blocks: 16 (a row of up to
 // 16 heads in one workgroup) while a wave fits 128 registers, else 4.
-constexpr int waves_for(int kmax) { return kmax <= 16 ? kHeadsPerGroup : 4; }
+// Units of up to 64 blocks (few items each) finish 16 heads per workgroup;
+// longer units, whose merges take longer, spread a row over workgroups of 4
+// heads so that every CU takes a share.
+constexpr int waves_for(int kmax) { return kmax <= 1 ? kHeadsPerGroup : 4; }
 
 template <int KMAX>
 __global__ __launch_bounds__(kLanes *waves_for(KMAX)) void finish_kernel(const FinishParams p, int waves,

@@ -583,8 +583,9 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const SplitParams p) {
-  __shared__ int s_scan[kPlanThreads];
+  __shared__ int s_wave_total[kPlanThreads / 64];
   const int t = threadIdx.x;
+  const int lane = t & 63;
   const int U = p.rows * p.heads;
   const int per = (U + kPlanThreads - 1) / kPlanThreads;
   const int u0 = min(U, t * per), u1 = min(U, u0 + per);
@@ -596,13 +597,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const SplitParams p)
     const int nb = rp.bad ? 0 : (rp.n + kBlock - 1) / kBlock;
     int count = nb;
     if (!rp.bad && rp.eff == WISE_SPARSE) {
+      // popcount of the unit's support words, eight loads in flight at a time
       const uint32_t *sw = support_words(p, rp.slot, h);
+      const int nw = (nb + 31) >> 5;
       count = 0;
-      for (int w = 0; 32 * w < nb; ++w) {
-        uint32_t x = sw[w];
-        const int valid = nb - 32 * w;
-        if (valid < 32) x &= (1u << valid) - 1u;
-        count += __popc(x);
+      for (int w0 = 0; w0 < nw; w0 += 8) {
+        uint32_t x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = w0 + j < nw ? sw[w0 + j] : 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int valid = nb - 32 * (w0 + j);
+          count += __popc(valid < 32 ? x[j] & ((1u << max(valid, 0)) - 1u) : x[j]);
+        }
       }
     }
     const int items = (count + p.tiles_per_item - 1) / p.tiles_per_item;
@@ -614,22 +621,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const SplitParams p)
       if (rp.fallback && p.counters) atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
     }
   }
-  // exclusive scan of the per-thread item counts (Hillis-Steele in LDS)
-  s_scan[t] = local;
+  // exclusive scan of the per-thread item counts: within each wave, then
+  // the totals of the waves before it
+  const int incl = wave_inclusive_scan(local, lane);
+  if (lane == 63) s_wave_total[t >> 6] = incl;
   __syncthreads();
-  for (int d = 1; d < kPlanThreads; d <<= 1) {
-    const int y = t >= d ? s_scan[t - d] : 0;
-    __syncthreads();
-    s_scan[t] += y;
-    __syncthreads();
-  }
-  int at = s_scan[t] - local;
+  int before = 0;
+  for (int wv = 0; wv < (t >> 6); ++wv) before += s_wave_total[wv];
+  int at = before + incl - local;
   for (int u = u0; u < u1; ++u) {
     const int items = p.unit_items[u];
     for (int kk = 0; kk < items; ++kk) p.item_list[at + kk] = (static_cast<uint32_t>(u) << kItemBits) | kk;
     at += items;
   }
-  if (t == kPlanThreads - 1) *p.n_items = s_scan[t];
+  if (t == kPlanThreads - 1) *p.n_items = before + incl;
 }
 
 // ---------------------------------------------------------------------------
