@@ -142,7 +142,7 @@ void state_record_layout(int layers, int heads, int words, size_t *tags_offset, 
 // fused = static grid of one workgroup per unit that also runs the unit's
 // finish (merge, selection, support, row bookkeeping).
 // cus = compute units of the current device (sizes the persistent grid);
-// ev_begin / ev_end (optional) are recorded right around the split kernel.
+// ev_begin / ev_end (optional) are stamped with the split kernel's start and stop.
 hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, bool fused,
                         int cus, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 

@@ -28,6 +28,8 @@
 //    runs in base 2 on scores pre-scaled by scale*log2(e).  Every reduction
 //    is a fixed butterfly, so all lanes hold bitwise-identical statistics and
 //    a row's result does not depend on the other rows of the launch.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "wise_internal.h"
@@ -687,6 +689,19 @@ static int listed_groups_per_cu() {
   return cache[dev];
 }
 
+// Launch of one split kernel.  With timing events, through the launch that
+// stamps them with the kernel's own start and stop (hipExtLaunchKernel), so
+// they measure the kernel rather than the queue around it.
+template <typename... Args, typename F = void (*)(Args...)>
+static hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t stream, hipEvent_t ev_begin,
+                               hipEvent_t ev_end, Args... args) {
+  if (ev_begin)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev_begin, ev_end, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
+
 template <bool kBf16, int D>
 static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, bool fused, int cus,
                                hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
@@ -698,42 +713,35 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, b
         (static_cast<int64_t>(p.rows) * p.heads * p.items_per_unit + kWavesPerGroup - 1) / kWavesPerGroup;
     const int groups = static_cast<int>(std::min<int64_t>(slot_groups, static_cast<int64_t>(cus) * per_cu));
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
-    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((split_listed_kernel<kBf16, D>), dim3(groups), block, 0, stream, p);
-  } else {
-    const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
-    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipErrorInvalidValue;
-    if (fused) {
-      // one workgroup per unit, one wave per item slot
-      const dim3 units(static_cast<unsigned>(p.rows) * p.heads);
-      if (k_only) {
-        if (p.items_per_unit <= 4)
-          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 4, true>), units, dim3(64 * 4), 0, stream, p);
-        else if (p.items_per_unit <= 8)
-          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 8, true>), units, dim3(64 * 8), 0, stream, p);
-        else if constexpr (kBf16 || D == 64)
-          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 16, true>), units, dim3(64 * 16), 0, stream, p);
-        else
-          return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
-      } else {
-        if (p.items_per_unit <= 4)
-          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 4, false>), units, dim3(64 * 4), 0, stream, p);
-        else if (p.items_per_unit <= 8)
-          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 8, false>), units, dim3(64 * 8), 0, stream, p);
-        else if constexpr (kBf16 || D == 64)
-          hipLaunchKernelGGL((split_fused_kernel<kBf16, D, 16, false>), units, dim3(64 * 16), 0, stream, p);
-        else
-          return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
-      }
-    } else if (k_only)
-      hipLaunchKernelGGL((split_static_kernel<kBf16, D, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((split_static_kernel<kBf16, D, false>), grid, block, 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_timed(split_listed_kernel<kBf16, D>, dim3(groups), block, stream, ev_begin, ev_end, p);
   }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return hipErrorInvalidValue;
-  return hipSuccess;
+  if (fused) {
+    // one workgroup per unit, one wave per item slot
+    const dim3 units(static_cast<unsigned>(p.rows) * p.heads);
+    if (k_only) {
+      if (p.items_per_unit <= 4)
+        return launch_timed(split_fused_kernel<kBf16, D, 4, true>, units, dim3(64 * 4), stream, ev_begin, ev_end, p);
+      if (p.items_per_unit <= 8)
+        return launch_timed(split_fused_kernel<kBf16, D, 8, true>, units, dim3(64 * 8), stream, ev_begin, ev_end, p);
+      if constexpr (kBf16 || D == 64)
+        return launch_timed(split_fused_kernel<kBf16, D, 16, true>, units, dim3(64 * 16), stream, ev_begin, ev_end,
+                            p);
+      return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
+    }
+    if (p.items_per_unit <= 4)
+      return launch_timed(split_fused_kernel<kBf16, D, 4, false>, units, dim3(64 * 4), stream, ev_begin, ev_end, p);
+    if (p.items_per_unit <= 8)
+      return launch_timed(split_fused_kernel<kBf16, D, 8, false>, units, dim3(64 * 8), stream, ev_begin, ev_end, p);
+    if constexpr (kBf16 || D == 64)
+      return launch_timed(split_fused_kernel<kBf16, D, 16, false>, units, dim3(64 * 16), stream, ev_begin, ev_end,
+                          p);
+    return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
+  }
+  const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
+  if (k_only) return launch_timed(split_static_kernel<kBf16, D, true>, grid, block, stream, ev_begin, ev_end, p);
+  return launch_timed(split_static_kernel<kBf16, D, false>, grid, block, stream, ev_begin, ev_end, p);
 }
 
 hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, bool fused,

@@ -116,8 +116,10 @@ typedef struct wise_tag {
  *   tile_stats optional [rows, heads, ceil(max_ctx/32), 2] fp32: for every
  *             tile a row attends, (max scaled score, sum exp(score - max))
  *             in natural-log units; other entries are left untouched.
- *   ev_split_begin/end optional hipEvent_t recorded on `stream` right
- *             before and after the split-KV kernel (timing hook), or NULL.
+ *   ev_split_begin/end optional hipEvent_t (timing hook), or NULL: stamped
+ *             with the split-KV kernel's own start and stop by the launch
+ *             (hipExtLaunchKernel), so their elapsed time is the kernel's
+ *             duration.  Both or neither.
  * Supported: head_dim 64 or 128; page_size a power of two in [8, 4096];
  * max_ctx <= 65536; rows*heads <= 2^22.
  */
