@@ -206,3 +206,13 @@ def test_snapshot_bytes_and_validation(lib):
     assert snap(count=0, nbytes=0) == W.WISE_OK         # nothing to copy, nothing enqueued
     assert lib.wise_support_restore(ctypes.byref(s), 2, FAKE, 3, D, 3 * need - 8, None) == W.WISE_E_ARG
     assert lib.wise_support_restore(ctypes.byref(s), 2, FAKE, 0, D, 0, None) == W.WISE_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without libwise.so the binding raises; nothing falls back to a CPU path."""
+    monkeypatch.setattr(W, "_lib", None)
+    monkeypatch.setattr(W, "LIB_PATH", os.path.join(ROOT, "_no_such_dir", "libwise.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        W.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        W.wise_workspace_size(1, 1, 128, 64)
