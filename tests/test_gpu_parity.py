@@ -165,6 +165,18 @@ def test_small_launches(torch, dtype, d, ctxs):
     run_schedule(w)
 
 
+@pytest.mark.parametrize("heads,ctxs", [(1, (200, 1000)), (20, (300, 1024)), (20, (700, 3000)),
+                                        (256, (64, 128))])
+def test_head_counts(torch, heads, ctxs):
+    """One head; 20 heads (a fused row of more than 16 heads at 1K, rows of
+    several finish workgroups at 3K); 256 heads (beyond the fused kernel's
+    8-bit arrival count, so the two-kernel path)."""
+    w = synth.Workload(name=f"heads{heads}_{max(ctxs)}", rows=len(ctxs), heads=heads, head_dim=64,
+                       dtype="bf16", page_size=16, shuffle=True, alpha=6.0, seed=81, ctx_list=ctxs, hot=2,
+                       schedule=(1, 2, 3), eta=0.9)
+    run_schedule(w)
+
+
 def test_page_size_and_layout_invariance(torch):
     """Physical layout changes nothing: same bits for page sizes 8..64, a
     shuffled or identity block table, and [pages, P, H, d] storage."""
