@@ -158,9 +158,16 @@ __device__ __forceinline__ u32x4 load16(const char *p) {
 struct RowPlan {
   int row, n, req, eff, slot;
   bool bad, fallback;
+  uint32_t word;  // this lane's support word of (slot, head), when requested and the row asks for SPARSE
 };
 
-__device__ __forceinline__ RowPlan plan_row(const SplitParams &p, int r) {
+__device__ __forceinline__ const uint32_t *support_words(const SplitParams &p, int slot, int h);
+
+// Effective mode of row r.  With h >= 0, a row that requests SPARSE also
+// gets lane's support word of (slot, h) loaded here, issued together with
+// the tag loads instead of after the tag check (it is used only if the row
+// stays sparse).
+__device__ __forceinline__ RowPlan plan_row(const SplitParams &p, int r, int h = -1, int lane = 0) {
   RowPlan rp;
   rp.row = r;
   rp.n = p.ctx_len[r];
@@ -169,12 +176,17 @@ __device__ __forceinline__ RowPlan plan_row(const SplitParams &p, int r) {
   rp.eff = rp.req;
   rp.slot = r;
   rp.fallback = false;
+  rp.word = 0u;
   if (!rp.bad && rp.req != WISE_DENSE) {
     if (p.slot_of_row) rp.slot = p.slot_of_row[r];
     if (rp.slot < 0 || rp.slot >= p.slots) {
       rp.bad = true;
     } else if (rp.req == WISE_DISCOVER_UNION || rp.req == WISE_SPARSE) {
       const wise_tag *t = p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer;
+      if (h >= 0 && rp.req == WISE_SPARSE) {
+        const int nw = ((rp.n + kBlock - 1) / kBlock + 31) >> 5;
+        if (lane < nw) rp.word = support_words(p, rp.slot, h)[lane];
+      }
       const bool same = t->request == p.row_request[r] && t->position == p.row_position[r];
       const int need = rp.req == WISE_SPARSE ? p.required : 1;
       if (!(same && t->discoveries >= need)) {
@@ -190,15 +202,14 @@ __device__ __forceinline__ const uint32_t *support_words(const SplitParams &p, i
   return p.support + ((static_cast<int64_t>(slot) * p.layers + p.layer) * p.heads + h) * p.words;
 }
 
-// One wave: lane l < ceil(nb/32) holds support word l (bits past nb cleared);
-// incl = inclusive prefix of the words' popcounts; returns the set-bit count.
-__device__ __forceinline__ int support_scan(const SplitParams &p, int slot, int h, int nb, int lane,
-                                            uint32_t &word, int &incl) {
-  const uint32_t *sw = support_words(p, slot, h);
+// One wave: lane l < ceil(nb/32) holds support word l (raw, as loaded; bits
+// past nb are cleared here); incl = inclusive prefix of the words'
+// popcounts; returns the set-bit count.
+__device__ __forceinline__ int support_scan(uint32_t raw, int nb, int lane, uint32_t &word, int &incl) {
   const int nw = (nb + 31) >> 5;
   word = 0u;
   if (lane < nw) {
-    word = sw[lane];
+    word = raw;
     const int valid = nb - 32 * lane;
     if (valid < 32) word &= (1u << valid) - 1u;
   }
@@ -411,14 +422,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
     const int nb0 = (n0 >= 1 && n0 <= p.max_ctx) ? (n0 + kBlock - 1) / kBlock : 0;
     if (k >= (nb0 + p.tiles_per_item - 1) / p.tiles_per_item) return;
   }
-  const RowPlan rp = plan_row(p, r);
+  const RowPlan rp = plan_row(p, r, h, lane);
   const int nb = rp.bad ? 0 : (rp.n + kBlock - 1) / kBlock;
   const bool sparse = !rp.bad && rp.eff == WISE_SPARSE;
   uint32_t word = 0u;
   int incl = 0;
   // K-only calls have nothing to do for a row whose discovery window broke
   const int count = (kKOnly && rp.eff == WISE_DENSE) ? 0
-                    : sparse                         ? support_scan(p, rp.slot, h, nb, lane, word, incl)
+                    : sparse                         ? support_scan(rp.word, nb, lane, word, incl)
                                                      : nb;
   const int items = (count + p.tiles_per_item - 1) / p.tiles_per_item;
   if (k == 0 && lane == 0) {
@@ -555,14 +566,14 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   const int u = blockIdx.x;  // unit = (row, head); units of a row spread over the XCDs
   const int r = u / p.heads;
   const int h = u - r * p.heads;
-  const RowPlan rp = plan_row(p, r);
+  const RowPlan rp = plan_row(p, r, h, lane);
   const int nb = rp.bad ? 0 : (rp.n + kBlock - 1) / kBlock;
   const bool sparse = !rp.bad && rp.eff == WISE_SPARSE;
   uint32_t word = 0u;
   int incl = 0;
   // K-only calls have nothing to do for a row whose discovery window broke
   const int count = (kKOnly && rp.eff == WISE_DENSE) ? 0
-                    : sparse                         ? support_scan(p, rp.slot, h, nb, lane, word, incl)
+                    : sparse                         ? support_scan(rp.word, nb, lane, word, incl)
                                                      : nb;
   // the unit's list entries spread evenly over the workgroup's waves (the
   // partials stay in LDS, so the item size need not match the workspace's)
@@ -657,14 +668,18 @@ void split_listed_kernel(const SplitParams p) {
     const int r = u / p.heads;
     const int h = u - r * p.heads;
     const int n = p.ctx_len[r];
-    const int eff = p.row_code[r] & 0xF;
-    const bool sparse = eff == WISE_SPARSE;
-    int slot = r;
-    if (sparse && p.slot_of_row) slot = p.slot_of_row[r];
+    const int code = p.row_code[r];
+    const int slot = p.slot_of_row ? p.slot_of_row[r] : r;
+    // the support word is loaded with the row code, before the mode is known
+    // (a slot out of range is not read; only sparse rows use the word)
+    const int nb = (n + kBlock - 1) / kBlock;
+    const int nw = min((nb + 31) >> 5, p.words);
+    uint32_t raw = 0u;
+    if (slot >= 0 && slot < p.slots && lane < nw) raw = support_words(p, slot, h)[lane];
+    const bool sparse = (code & 0xF) == WISE_SPARSE;
     uint32_t word = 0u;
     int incl = 0;
-    const int nb = (n + kBlock - 1) / kBlock;
-    const int count = sparse ? support_scan(p, slot, h, nb, lane, word, incl) : nb;
+    const int count = sparse ? support_scan(raw, nb, lane, word, incl) : nb;
     run_item<kBf16, D, false>(p, u, r, h, k, n, sparse, count, word, incl, lane, s_tiles[wave], p.tiles_per_item);
   }
 }
