@@ -21,6 +21,14 @@ int tiles_per_item(int max_blocks, int64_t units) {
   return t;
 }
 
+int long_tiles_per_item(const Layout &L) {
+  if (L.tiles_per_item != 8) return L.tiles_per_item;  // a small launch keeps its cut
+  const int64_t units = static_cast<int64_t>(L.rows) * L.heads;
+  for (int t = kLongTiles; t > 8; t >>= 1)
+    if (units * ((L.max_blocks + t - 1) / t) >= kLongItemMinWaves) return t;
+  return 8;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 bool make_layout(int rows, int heads, int head_dim, int max_ctx, Layout *L) {
@@ -216,6 +224,13 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
   const bool fused = fused_finish_shape(L, a->heads, a->dtype);
   p.lse = lse;
   const bool listed = !fused && (row_mode != nullptr || uniform_mode == WISE_SPARSE) && p.chunk_groups > 1;
+  // a static call with no sparse rows: longer items for large launches (the
+  // finish merges unit_items[u] partials at the workspace's slot stride)
+  if (!fused && !listed && row_mode == nullptr && uniform_mode != WISE_SPARSE) {
+    p.tiles_per_item = long_tiles_per_item(L);
+    const int items = (L.max_blocks + p.tiles_per_item - 1) / p.tiles_per_item;
+    p.chunk_groups = (items + kWavesPerGroup - 1) / kWavesPerGroup;
+  }
   const int cus = listed ? compute_units() : 0;
   if (listed && cus <= 0) return WISE_E_HIP;
   if (launch_split(p, a->dtype, a->head_dim, listed, k_only, fused, cus,

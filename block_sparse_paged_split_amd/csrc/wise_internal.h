@@ -12,7 +12,7 @@ namespace wise {
 
 constexpr int kBlock = WISE_BLOCK;     // tokens per tile / selection block
 constexpr int kWavesPerGroup = 4;      // waves per split workgroup (one work item each)
-constexpr int kMaxTilesPerItem = 16;   // upper bound of tiles per work item
+constexpr int kMaxTilesPerItem = 16;   // tiles per work item (dense items of static calls: kLongTiles)
 constexpr int kMaxCtx = 65536;         // tokens; 2048 blocks, 64 support words
 constexpr int kMaxBlocks = kMaxCtx / kBlock;
 constexpr int kMaxWords = kMaxBlocks / 32;
@@ -34,6 +34,15 @@ constexpr int64_t kSmallLaunchItems = 1024;  // below this many 8-tile items a l
 constexpr int kMaxFusedItems = 16;            // items (waves) of one fused split + finish workgroup
 constexpr int kMaxFusedBlocks = 64;           // blocks of a fused unit (one per lane in its selection)
 
+// Calls with no sparse rows run on the static grid with longer items when
+// the launch stays large: every item leaves a partial (m, l, acc) in HBM,
+// and those writes, interleaved with the K/V stream, cost far more than
+// their bytes (about 5% of a 4K-8K launch at eight tiles per item).  Mixed
+// calls keep eight tiles, as the split design prescribes, so that a dense
+// row among sparse ones does not set the launch latency.
+constexpr int kLongTiles = 32;                 // longest item (stats and list entries stay one per lane)
+constexpr int64_t kLongItemMinWaves = 4096;    // waves a launch keeps when its items grow
+
 struct Layout {
   int rows, heads, head_dim, max_ctx, max_blocks, tiles_per_item, items_per_unit;
   size_t off_row_code, off_row_done, off_unit_items, off_n_items, off_item_list, off_part_ml, off_part_acc,
@@ -41,6 +50,9 @@ struct Layout {
 };
 // Returns false if the sizes are outside the supported range.
 bool make_layout(int rows, int heads, int head_dim, int max_ctx, Layout *L);
+// Tiles per item of a static call with no sparse rows (kLongTiles, 16 or
+// the layout's own).
+int long_tiles_per_item(const Layout &L);
 
 struct SplitParams {
   const void *q, *k, *v;

@@ -29,10 +29,17 @@ constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E;
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128, kRowRor12 = 0x12C;
 
-// Value held by lane (lane ^ M).
+// Value held by lane (lane ^ M).  For M = 16 and 32, v_permlane16_swap
+// (v_permlane32_swap) with both operands x returns x of the lower lane of
+// each pair (lane with bit M clear) first and x of the upper lane second, in
+// both lanes of the pair; each lane keeps its partner's.
 template <int M>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
-  if constexpr (M == 1) {
+  if constexpr (M == 16 || M == 32) {
+    const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                           : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & M) ? r[0] : r[1];
+  } else if constexpr (M == 1) {
     return dpp32<kQuadSwap1>(x);
   } else if constexpr (M == 2) {
     return dpp32<kQuadSwap2>(x);
@@ -42,7 +49,8 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
   } else if constexpr (M == 8) {
     return dpp32<kRowRor8>(x);
   } else {
-    return static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), M));
+    static_assert(M < 0, "lane distance must be 1, 2, 4, 8, 16 or 32");
+    return x;
   }
 }
 template <int M>

@@ -18,16 +18,22 @@
 //    waves per workgroup over every (unit, item) slot, finished by the
 //    finish kernel), and the listed grid (persistent waves over the compact
 //    item list a one-workgroup plan kernel builds, for calls with sparse
-//    rows whose units span several workgroups).
+//    rows whose units span several workgroups).  Items keep about eight
+//    tiles wherever sparse rows may share the launch; a call with no sparse
+//    rows whose launch stays large runs 16- or 32-tile items instead, since
+//    each item's partial (m, l, acc) written to HBM amid the K/V stream
+//    costs far more than its bytes.
 //  * A 32-token K (or V) tile is read with 16-byte loads in which each load
 //    instruction covers TPI whole tokens contiguously (1 KB per wave for
 //    bf16 d=128): lane = (token subgroup g, 16-byte dim chunk c).  Every K
 //    and V load of a tile is issued before any arithmetic.
 //  * q.k uses v_dot2 (bf16 pairs, fp32 accumulate) or fp32 FMA, reduced
-//    across the LPT lanes of a token with DPP row rotations.  Online softmax
-//    runs in base 2 on scores pre-scaled by scale*log2(e).  Every reduction
-//    is a fixed butterfly, so all lanes hold bitwise-identical statistics and
-//    a row's result does not depend on the other rows of the launch.
+//    across the LPT lanes of a token with DPP row rotations; lanes 16 and 32
+//    apart exchange through v_permlane16_swap / v_permlane32_swap (register
+//    swaps, no LDS round trip).  Online softmax runs in base 2 on scores
+//    pre-scaled by scale*log2(e).  Every reduction is a fixed butterfly, so
+//    all lanes hold bitwise-identical statistics and a row's result does not
+//    depend on the other rows of the launch.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -59,6 +65,23 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
+// Lanes l and l ^ 16 (or l ^ 32) exchanged in registers: v_permlane16_swap
+// (v_permlane32_swap) with both operands x leaves x of the lower partner in
+// the first result and x of the upper partner in the second, in both lanes,
+// so a combine of the pair gives bitwise the same value in both.
+__device__ __forceinline__ float2 pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum16(float x) { const float2 q = pair16(x); return q.x + q.y; }
+__device__ __forceinline__ float sum32(float x) { const float2 q = pair32(x); return q.x + q.y; }
+__device__ __forceinline__ float max16(float x) { const float2 q = pair16(x); return fmaxf(q.x, q.y); }
+__device__ __forceinline__ float max32(float x) { const float2 q = pair32(x); return fmaxf(q.x, q.y); }
+
 // Sum over aligned groups of LPT consecutive lanes; every lane of a group
 // gets the bitwise-same total.
 template <int LPT>
@@ -72,7 +95,7 @@ __device__ __forceinline__ float lane_group_sum(float x) {
     x += dpp<0x124>(x);  // row_ror:4
     x += dpp<0x122>(x);  // row_ror:2
     x += dpp<0x121>(x);  // row_ror:1
-    if constexpr (LPT == 32) x += __shfl_xor(x, 16);
+    if constexpr (LPT == 32) x = sum16(x);
   }
   return x;
 }
@@ -81,16 +104,14 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 template <int LPT>
 __device__ __forceinline__ float subgroup_max(float x) {
   if constexpr (LPT <= 8) x = fmaxf(x, dpp<0x128>(x));  // partner lane l ^ 8 within the row
-  if constexpr (LPT <= 16) x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  if constexpr (LPT <= 16) x = max16(x);
+  return max32(x);
 }
 template <int LPT>
 __device__ __forceinline__ float subgroup_sum(float x) {
   if constexpr (LPT <= 8) x += dpp<0x128>(x);
-  if constexpr (LPT <= 16) x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  if constexpr (LPT <= 16) x = sum16(x);
+  return sum32(x);
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
@@ -396,8 +417,9 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
 // Static grid: one wave per (unit, item slot); every wave plans its own item.
 // Used for calls the fused kernel does not cover that have no sparse rows
 // (every unit's item count then follows from its context length, so nearly
-// every slot holds work), and for sparse calls whose units fit one
-// workgroup but do not fuse.
+// every slot holds work; such calls may run longer items, tiles_per_item up
+// to kLongTiles), and for sparse calls whose units fit one workgroup but do
+// not fuse.
 // ---------------------------------------------------------------------------
 template <bool kBf16, int D, bool kKOnly>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const SplitParams p) {

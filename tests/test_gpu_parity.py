@@ -177,6 +177,34 @@ def test_head_counts(torch, heads, ctxs):
     run_schedule(w)
 
 
+@pytest.mark.parametrize("rows,heads,tiles", [(32, 16, 16), (32, 32, 32)])
+def test_long_items(torch, rows, heads, tiles):
+    """Calls with no sparse rows whose launch stays large run 16- or 32-tile
+    items on the static grid (a quarter or half of the partials); sampled rows
+    of every depth -- dense, discover, union, and the sparse depth on the
+    listed grid's 8-tile items -- against the oracle.  The same dense rows in
+    a call with a per-row mode array (8-tile items) agree to fp32 rounding."""
+    w = synth.Workload(name=f"long{tiles}_{rows}x{heads}", rows=rows, heads=heads, head_dim=128, dtype="bf16",
+                       page_size=16, shuffle=True, alpha=2.5, seed=93, ctx=4096, hot=6,
+                       schedule=(W.WISE_DENSE, W.WISE_DISCOVER, W.WISE_DISCOVER_UNION, W.WISE_SPARSE))
+    units = rows * heads
+    assert units * (128 // tiles) >= 4096 and (tiles == 32 or units * (128 // 32) < 4096)
+    reps, state = run_schedule(w, rows=[0, 7, rows - 1])
+    assert all(r.counters[W.CTR_FALLBACKS] == 0 and r.counters[W.CTR_ERRORS] == 0 for r in reps)
+    li, dev = _one_layer(w, 0)
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    harness.call(dev, ws, W.WISE_DENSE)
+    torch.cuda.synchronize()
+    long_out = dev.out.clone()
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    harness.call(dev, ws, W.WISE_SPARSE, st, required=1,
+                 row_mode=torch.full((w.rows,), W.WISE_DENSE, dtype=torch.uint8, device=dev.out.device))
+    torch.cuda.synchronize()
+    diff = (dev.out - long_out).abs().max().item()
+    say(f"   long vs 8-tile items: max |diff| {diff:.2e}")
+    assert diff <= 1e-5 * max(1.0, long_out.abs().max().item())
+
+
 def test_page_size_and_layout_invariance(torch):
     """Physical layout changes nothing: same bits for page sizes 8..64, a
     shuffled or identity block table, and [pages, P, H, d] storage."""
