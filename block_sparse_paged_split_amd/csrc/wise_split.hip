@@ -185,12 +185,31 @@ struct RowPlan {
 __device__ __forceinline__ const uint32_t *support_words(const SplitParams &p, int slot, int h);
 
 // Effective mode of row r.  With h >= 0, a row that requests SPARSE also
-// gets lane's support word of (slot, h) loaded here, issued together with
-// the tag loads instead of after the tag check (it is used only if the row
-// stays sparse).
+// gets lane's support word of (slot, h).  Every load the plan may need is
+// issued before any of them is used: when rows map to slots one to one (no
+// slot_of_row), the slot is known without a load, so the tag, the row's
+// (request, position) and the support word are issued first, whatever the
+// mode turns out to be, and the context length and the mode after them;
+// with slot_of_row the state follows that one load.  The tag is compared
+// field by field without short-circuiting, so its words arrive in one round
+// trip.
 __device__ __forceinline__ RowPlan plan_row(const SplitParams &p, int r, int h = -1, int lane = 0) {
   RowPlan rp;
   rp.row = r;
+  const bool ident = p.slot_of_row == nullptr;
+  int64_t t_req = 0, t_pos = 0, r_req = 0, r_pos = 0;
+  int t_disc = 0;
+  uint32_t word = 0u;
+  auto load_state = [&](int sl) {
+    const wise_tag *t = p.tags + static_cast<int64_t>(sl) * p.layers + p.layer;
+    t_req = t->request;
+    t_pos = t->position;
+    t_disc = t->discoveries;
+    r_req = p.row_request[r];
+    r_pos = p.row_position[r];
+    if (h >= 0 && lane < p.words) word = support_words(p, sl, h)[lane];
+  };
+  if (p.tags != nullptr && ident && r < p.slots) load_state(r);
   rp.n = p.ctx_len[r];
   rp.req = p.row_mode ? static_cast<int>(p.row_mode[r]) : p.uniform_mode;
   rp.bad = rp.n < 1 || rp.n > p.max_ctx || rp.req < WISE_DENSE || rp.req > WISE_SPARSE;
@@ -199,21 +218,22 @@ __device__ __forceinline__ RowPlan plan_row(const SplitParams &p, int r, int h =
   rp.fallback = false;
   rp.word = 0u;
   if (!rp.bad && rp.req != WISE_DENSE) {
-    if (p.slot_of_row) rp.slot = p.slot_of_row[r];
-    if (rp.slot < 0 || rp.slot >= p.slots) {
+    int slot = r;
+    if (!ident) {
+      slot = p.slot_of_row[r];
+      if (slot >= 0 && slot < p.slots) load_state(slot);
+    }
+    rp.slot = slot;
+    if (slot < 0 || slot >= p.slots) {
       rp.bad = true;
     } else if (rp.req == WISE_DISCOVER_UNION || rp.req == WISE_SPARSE) {
-      const wise_tag *t = p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer;
-      if (h >= 0 && rp.req == WISE_SPARSE) {
-        const int nw = ((rp.n + kBlock - 1) / kBlock + 31) >> 5;
-        if (lane < nw) rp.word = support_words(p, rp.slot, h)[lane];
-      }
-      const bool same = t->request == p.row_request[r] && t->position == p.row_position[r];
+      const bool same = (t_req == r_req) & (t_pos == r_pos);
       const int need = rp.req == WISE_SPARSE ? p.required : 1;
-      if (!(same && t->discoveries >= need)) {
+      if (!(same & (t_disc >= need))) {
         rp.eff = WISE_DENSE;
         rp.fallback = true;
       }
+      if (rp.req == WISE_SPARSE) rp.word = word;
     }
   }
   return rp;
@@ -683,8 +703,12 @@ void split_listed_kernel(const SplitParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int stride = gridDim.x * kWavesPerGroup;
   const int n_items = *p.n_items;
-  for (int i = blockIdx.x * kWavesPerGroup + wave; i < n_items; i += stride) {
-    const uint32_t it = p.item_list[i];
+  int i = blockIdx.x * kWavesPerGroup + wave;
+  uint32_t it_next = i < n_items ? p.item_list[i] : 0u;
+  for (; i < n_items; i += stride) {
+    // this wave's next list entry is fetched one item ahead
+    const uint32_t it = it_next;
+    if (i + stride < n_items) it_next = p.item_list[i + stride];
     const int u = static_cast<int>(it >> kItemBits);
     const int k = static_cast<int>(it & ((1u << kItemBits) - 1u));
     const int r = u / p.heads;
@@ -692,12 +716,12 @@ void split_listed_kernel(const SplitParams p) {
     const int n = p.ctx_len[r];
     const int code = p.row_code[r];
     const int slot = p.slot_of_row ? p.slot_of_row[r] : r;
-    // the support word is loaded with the row code, before the mode is known
-    // (a slot out of range is not read; only sparse rows use the word)
+    // the support word is loaded with the context and the row code, before
+    // either is known (a slot out of range is not read; only sparse rows use
+    // the word, and support_scan drops the words past the context)
     const int nb = (n + kBlock - 1) / kBlock;
-    const int nw = min((nb + 31) >> 5, p.words);
     uint32_t raw = 0u;
-    if (slot >= 0 && slot < p.slots && lane < nw) raw = support_words(p, slot, h)[lane];
+    if (slot >= 0 && slot < p.slots && lane < p.words) raw = support_words(p, slot, h)[lane];
     const bool sparse = (code & 0xF) == WISE_SPARSE;
     uint32_t word = 0u;
     int incl = 0;
