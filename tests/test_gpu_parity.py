@@ -177,14 +177,15 @@ def test_head_counts(torch, heads, ctxs):
     run_schedule(w)
 
 
-@pytest.mark.parametrize("rows,heads,tiles", [(32, 16, 16), (32, 32, 32)])
-def test_long_items(torch, rows, heads, tiles):
+@pytest.mark.parametrize("rows,heads,tiles,dtype,d", [(32, 16, 16, "bf16", 128), (32, 32, 32, "bf16", 128),
+                                                   (16, 32, 16, "f32", 64)])
+def test_long_items(torch, rows, heads, tiles, dtype, d):
     """Calls with no sparse rows whose launch stays large run 16- or 32-tile
     items on the static grid (a quarter or half of the partials); sampled rows
     of every depth -- dense, discover, union, and the sparse depth on the
     listed grid's 8-tile items -- against the oracle.  The same dense rows in
     a call with a per-row mode array (8-tile items) agree to fp32 rounding."""
-    w = synth.Workload(name=f"long{tiles}_{rows}x{heads}", rows=rows, heads=heads, head_dim=128, dtype="bf16",
+    w = synth.Workload(name=f"long{tiles}_{rows}x{heads}_{dtype}{d}", rows=rows, heads=heads, head_dim=d, dtype=dtype,
                        page_size=16, shuffle=True, alpha=2.5, seed=93, ctx=4096, hot=6,
                        schedule=(W.WISE_DENSE, W.WISE_DISCOVER, W.WISE_DISCOVER_UNION, W.WISE_SPARSE))
     units = rows * heads
