@@ -295,6 +295,32 @@ def test_device_data_errors(torch):
     # row 1's bad page sits in block 1: NaN only for heads whose support holds it
 
 
+@pytest.mark.parametrize("ctx", [1000, 3000])
+def test_slot_indirection(torch, ctx):
+    """Rows mapped to slots of a larger pool through slot_of_row (the state
+    of each slot read after that one load): a full discover, union, sparse
+    schedule against the oracle, fused (1K) and static + listed (3K) shapes;
+    slots no row maps to keep their contents."""
+    w = synth.Workload(name=f"slots_{ctx}", rows=6, heads=4, head_dim=128, dtype="bf16", page_size=16,
+                       shuffle=True, alpha=4.0, seed=97, ctx=ctx, hot=3,
+                       schedule=(W.WISE_DISCOVER, W.WISE_DISCOVER_UNION, W.WISE_SPARSE))
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx, slots=16)
+    st.slot_of_row = torch.tensor([9, 3, 14, 0, 7, 12], dtype=torch.int32, device="cuda")
+    st.row_position.fill_(23)
+    st.support.fill_(0x5A5A5A5A)  # every slot starts with foreign bits
+    free = [sl for sl in range(16) if sl not in (9, 3, 14, 0, 7, 12)]
+    before = st.support[free].clone()
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    for depth, mode in enumerate(w.schedule):
+        say(f"[{w.name}] depth {depth} mode {mode} through slot_of_row")
+        li = synth.layer_inputs(w, depth)
+        dev = harness.upload(li, with_stats=True)
+        rep = check_call(w, li, dev, ws, st, mode=mode)
+        say(f"   max_abs {rep.max_abs:.2e} counters {rep.counters}")
+        assert rep.counters[W.CTR_FALLBACKS] == 0 and rep.counters[W.CTR_ERRORS] == 0
+    assert torch.equal(st.support[free], before)
+
+
 def test_graph_replay_matches_eager(torch):
     """A whole step captured in a HIP graph: every replay (with eager work and
     synchronisation in between) equals the eager step bit for bit."""
