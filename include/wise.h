@@ -188,10 +188,15 @@ wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
 /* Merge the splits of the preceding decode call into a->out; for discovery
  * rows run the eta selection, write/OR the support, update the tags and
  * the counters.  `a` and `s` must describe the same call as the decode
- * call (s == NULL after wise_decode_dense).  When every unit's work items
- * fit one split workgroup (ceil(ceil(max_ctx/32)/8) <= 4, i.e. max_ctx <=
- * 1024, and heads <= 255) the decode call has already done all of this in
- * the same kernel, and this call only validates its arguments. */
+ * call (s == NULL after wise_decode_dense).  When every (row, head)'s work
+ * items fit one split workgroup the decode call has already done all of
+ * this in the same kernel, and this call only validates its arguments:
+ * with heads <= 255, every call with max_ctx <= 1024, and small launches
+ * (fewer than 1024 eight-tile items over all rows and heads) with max_ctx
+ * <= 2048; for fp32 at head_dim 128 only launches of at least 1024 such
+ * items with max_ctx <= 1024, and small ones with max_ctx <= 256.  It is
+ * still required: which shapes finish inside the decode kernel is the
+ * library's choice and may change. */
 wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws,
                                size_t ws_bytes, void *stream);
 
