@@ -128,6 +128,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 
@@ -274,7 +275,11 @@ struct UnitLds {
   float2 *stats;    // [blocks] tile stats by block index (non-sparse items)
 };
 
-template <bool kBf16, int D, bool kKOnly>
+// kStreamPartials: the accumulator partial goes out as a nontemporal store
+// (the static grid, whose full 512-byte partials then disturb the K/V
+// stream less: 1-2% at 8K and on ragged batches; the listed grid measured
+// no better with it).
+template <bool kBf16, int D, bool kKOnly, bool kStreamPartials = false>
 __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int h, int k, int n, bool sparse,
                                          int count, uint32_t word, int incl, int lane, int *tiles, int T,
                                          const UnitLds *lds = nullptr) {
@@ -415,9 +420,15 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
     if (lane == 0) lds->ml[k] = ml;
   } else {
     if (!kKOnly && g == 0) {
-      float4 *dst = reinterpret_cast<float4 *>(p.part_acc + slot_idx * D + c * G::EPL);
+      f32x4 *dst = reinterpret_cast<f32x4 *>(p.part_acc + slot_idx * D + c * G::EPL);
 #pragma unroll
-      for (int e = 0; e < G::EPL; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      for (int e = 0; e < G::EPL; e += 4) {
+        const f32x4 v = {acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+        if constexpr (kStreamPartials)
+          __builtin_nontemporal_store(v, dst + e / 4);
+        else
+          dst[e / 4] = v;
+      }
     }
     if (lane == 0) p.part_ml[slot_idx] = ml;
   }
@@ -483,8 +494,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
     }
   }
   if (k >= items) return;
-  run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave],
-                             p.tiles_per_item);
+  run_item<kBf16, D, kKOnly, true>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave],
+                                   p.tiles_per_item);
 }
 
 // ---------------------------------------------------------------------------
