@@ -231,6 +231,9 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
     const int items = (L.max_blocks + p.tiles_per_item - 1) / p.tiles_per_item;
     p.chunk_groups = (items + kWavesPerGroup - 1) / kWavesPerGroup;
   }
+  // a listed call's plan kernel may lengthen the items by the same rule,
+  // from the tiles the call really attends
+  p.long_items = listed && L.tiles_per_item == 8;
   const int cus = listed ? compute_units() : 0;
   if (listed && cus <= 0) return WISE_E_HIP;
   if (launch_split(p, a->dtype, a->head_dim, listed, k_only, fused, cus,

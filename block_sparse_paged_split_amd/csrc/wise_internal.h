@@ -12,7 +12,7 @@ namespace wise {
 
 constexpr int kBlock = WISE_BLOCK;     // tokens per tile / selection block
 constexpr int kWavesPerGroup = 4;      // waves per split workgroup (one work item each)
-constexpr int kMaxTilesPerItem = 16;   // tiles per work item (dense items of static calls: kLongTiles)
+constexpr int kMaxTilesPerItem = 16;   // tiles per work item (long items of large calls: kLongTiles)
 constexpr int kMaxCtx = 65536;         // tokens; 2048 blocks, 64 support words
 constexpr int kMaxBlocks = kMaxCtx / kBlock;
 constexpr int kMaxWords = kMaxBlocks / 32;
@@ -34,12 +34,14 @@ constexpr int64_t kSmallLaunchItems = 1024;  // below this many 8-tile items a l
 constexpr int kMaxFusedItems = 16;            // items (waves) of one fused split + finish workgroup
 constexpr int kMaxFusedBlocks = 64;           // blocks of a fused unit (one per lane in its selection)
 
-// Calls with no sparse rows run on the static grid with longer items when
-// the launch stays large: every item leaves a partial (m, l, acc) in HBM,
-// and those writes, interleaved with the K/V stream, cost far more than
-// their bytes (about 5% of a 4K-8K launch at eight tiles per item).  Mixed
-// calls keep eight tiles, as the split design prescribes, so that a dense
-// row among sparse ones does not set the launch latency.
+// Large launches run longer items: every item leaves a partial (m, l, acc)
+// in HBM, and those writes, interleaved with the K/V stream, cost far more
+// than their bytes (about 5% of a 4K-8K launch at eight tiles per item).
+// Calls with no sparse rows take the length on the host from the causal
+// tiles of max_ctx; calls with sparse rows take it in the plan kernel from
+// the tiles they really attend, by the same rule.  Launches below the
+// threshold keep eight tiles, as the split design prescribes, so that a
+// dense row among sparse ones does not set the launch latency.
 constexpr int kLongTiles = 32;                 // longest item (stats and list entries stay one per lane)
 constexpr int64_t kLongItemMinWaves = 4096;    // waves a launch keeps when its items grow
 
@@ -63,6 +65,7 @@ struct SplitParams {
   int32_t rows, heads, max_ctx, max_blocks, num_pages, page_shift;
   float qk_scale_log2;  // softmax scale * log2(e)
   int32_t tiles_per_item, items_per_unit, chunk_groups;
+  int32_t long_items;  // listed calls: the plan kernel may lengthen items to 16 or 32 tiles
   // requested modes
   const uint8_t *row_mode;  // NULL: every row uniform_mode
   int32_t uniform_mode;
@@ -82,7 +85,7 @@ struct SplitParams {
   // workspace and optional export
   int32_t *row_code, *unit_items;
   unsigned long long *row_done;
-  int32_t *n_items;      // live items in item_list (calls with sparse rows)
+  int32_t *n_items;      // [0] live items in item_list, [1] their tiles per item (calls with sparse rows)
   uint32_t *item_list;   // unit << kItemBits | item
   float2 *part_ml;
   float *part_acc;

@@ -19,10 +19,11 @@
 //    finish kernel), and the listed grid (persistent waves over the compact
 //    item list a one-workgroup plan kernel builds, for calls with sparse
 //    rows whose units span several workgroups).  Items keep about eight
-//    tiles wherever sparse rows may share the launch; a call with no sparse
-//    rows whose launch stays large runs 16- or 32-tile items instead, since
-//    each item's partial (m, l, acc) written to HBM amid the K/V stream
-//    costs far more than its bytes.
+//    tiles unless the launch is large enough to outlast any one item many
+//    times over; then they grow to 16 or 32 tiles (decided on the host for
+//    calls with no sparse rows, in the plan kernel from the attended tiles
+//    otherwise), since each item's partial (m, l, acc) written to HBM amid
+//    the K/V stream costs far more than its bytes.
 //  * A 32-token K (or V) tile is read with 16-byte loads in which each load
 //    instruction covers TPI whole tokens contiguously (1 KB per wave for
 //    bf16 d=128): lane = (token subgroup g, 16-byte dim chunk c).  Every K
@@ -275,14 +276,14 @@ struct UnitLds {
   float2 *stats;    // [blocks] tile stats by block index (non-sparse items)
 };
 
-// kStreamPartials: the accumulator partial goes out as a nontemporal store
-// (the static grid, whose full 512-byte partials then disturb the K/V
-// stream less: 1-2% at 8K and on ragged batches; the listed grid measured
-// no better with it).
-template <bool kBf16, int D, bool kKOnly, bool kStreamPartials = false>
+// stream_partials: the accumulator partial goes out as a nontemporal store,
+// which disturbs the K/V stream less behind long items (1-2% at 8K and on
+// ragged batches, static and listed grids alike) but costs the listed
+// grid's eight-tile items about as much (mixed 4K launch).
+template <bool kBf16, int D, bool kKOnly>
 __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int h, int k, int n, bool sparse,
                                          int count, uint32_t word, int incl, int lane, int *tiles, int T,
-                                         const UnitLds *lds = nullptr) {
+                                         const UnitLds *lds = nullptr, bool stream_partials = false) {
   using G = Geo<kBf16, D>;
   const int first = k * T;
   const int ntiles = min(T, count - first);
@@ -424,7 +425,7 @@ __device__ __forceinline__ void run_item(const SplitParams &p, int u, int r, int
 #pragma unroll
       for (int e = 0; e < G::EPL; e += 4) {
         const f32x4 v = {acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
-        if constexpr (kStreamPartials)
+        if (stream_partials)
           __builtin_nontemporal_store(v, dst + e / 4);
         else
           dst[e / 4] = v;
@@ -494,8 +495,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
     }
   }
   if (k >= items) return;
-  run_item<kBf16, D, kKOnly, true>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave],
-                                   p.tiles_per_item);
+  run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[wave], p.tiles_per_item,
+                             nullptr, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -643,20 +644,29 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
 
 // ---------------------------------------------------------------------------
 // Plan kernel (one workgroup) for calls with sparse rows: effective modes,
-// per-unit item counts, and the compact list of live items, so that the
-// split grid carries no empty item slots.
+// per-unit tile counts, the call's item length, per-unit item counts, and
+// the compact list of live items, so that the split grid carries no empty
+// item slots.  The item length follows the rule of calls with no sparse
+// rows, applied to the tiles the call really attends: 32 tiles when the
+// launch still has at least kLongItemMinWaves items of 32, else 16 on the
+// same condition, else eight.  A launch that large outlasts any one item
+// many times over, so a dense row among sparse ones cannot set its length,
+// while a smaller launch keeps the eight-tile items the split design
+// prescribes.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanRegUnits = 4;  // units per thread whose tile counts stay in registers
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const SplitParams p) {
   __shared__ int s_wave_total[kPlanThreads / 64];
+  __shared__ int s_wave_long[2][kPlanThreads / 64];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int U = p.rows * p.heads;
   const int per = (U + kPlanThreads - 1) / kPlanThreads;
   const int u0 = min(U, t * per), u1 = min(U, u0 + per);
-  int local = 0;
-  for (int u = u0; u < u1; ++u) {
+  // tiles a unit attends (its item count is fixed once the item length is)
+  auto unit_tiles = [&](int u) -> int {
     const int r = u / p.heads;
     const int h = u - r * p.heads;
     const RowPlan rp = plan_row(p, r);
@@ -678,42 +688,107 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const SplitParams p)
         }
       }
     }
-    const int items = (count + p.tiles_per_item - 1) / p.tiles_per_item;
-    p.unit_items[u] = items;
-    local += items;
     if (h == 0) {
       p.row_code[r] = encode_row(rp.bad ? kRowError : rp.eff, rp.req);
       p.row_done[r] = 0ull;
       if (rp.fallback && p.counters) atomicAdd(p.counters + WISE_CTR_FALLBACKS, 1ull);
     }
+    return count;
+  };
+  int cnt[kPlanRegUnits];
+  int n32 = 0, n16 = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanRegUnits; ++j) {
+    cnt[j] = u0 + j < u1 ? unit_tiles(u0 + j) : 0;
+    n32 += (cnt[j] + 31) >> 5;
+    n16 += (cnt[j] + 15) >> 4;
   }
-  // exclusive scan of the per-thread item counts: within each wave, then
-  // the totals of the waves before it
-  const int incl = wave_inclusive_scan(local, lane);
-  if (lane == 63) s_wave_total[t >> 6] = incl;
+  for (int u = u0 + kPlanRegUnits; u < u1; ++u) {
+    const int c = unit_tiles(u);
+    p.unit_items[u] = c;  // tile count until the item length is known
+    n32 += (c + 31) >> 5;
+    n16 += (c + 15) >> 4;
+  }
+  int T = p.tiles_per_item;
+  if (p.long_items) {
+    const int w32 = __builtin_amdgcn_readlane(wave_inclusive_scan(n32, lane), 63);
+    const int w16 = __builtin_amdgcn_readlane(wave_inclusive_scan(n16, lane), 63);
+    if (lane == 0) {
+      s_wave_long[0][t >> 6] = w32;
+      s_wave_long[1][t >> 6] = w16;
+    }
+    __syncthreads();
+    int tot32 = 0, tot16 = 0;
+    for (int wv = 0; wv < kPlanThreads / 64; ++wv) {
+      tot32 += s_wave_long[0][wv];
+      tot16 += s_wave_long[1][wv];
+    }
+    T = tot32 >= kLongItemMinWaves ? 32 : tot16 >= kLongItemMinWaves ? 16 : T;
+  }
+  // The list holds every unit's full-length items first, in unit order,
+  // then the shorter last items of the units whose tile count T does not
+  // divide.
+  int full = 0, tails = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanRegUnits; ++j) {
+    full += cnt[j] / T;
+    tails += cnt[j] % T != 0;
+  }
+  for (int u = u0 + kPlanRegUnits; u < u1; ++u) {
+    const int c = p.unit_items[u];
+    full += c / T;
+    tails += c % T != 0;
+  }
+  // exclusive scans of the per-thread full and tail counts: within each
+  // wave, then the totals of the waves before it
+  const int incl_full = wave_inclusive_scan(full, lane);
+  const int incl_tails = wave_inclusive_scan(tails, lane);
+  if (lane == 63) {
+    s_wave_total[t >> 6] = incl_full;
+    s_wave_long[0][t >> 6] = incl_tails;
+  }
   __syncthreads();
-  int before = 0;
-  for (int wv = 0; wv < (t >> 6); ++wv) before += s_wave_total[wv];
-  int at = before + incl - local;
-  for (int u = u0; u < u1; ++u) {
-    const int items = p.unit_items[u];
-    for (int kk = 0; kk < items; ++kk) p.item_list[at + kk] = (static_cast<uint32_t>(u) << kItemBits) | kk;
-    at += items;
+  int before_full = 0, all_full = 0, before_tails = 0, all_tails = 0;
+  for (int wv = 0; wv < kPlanThreads / 64; ++wv) {
+    const bool earlier = wv < (t >> 6);
+    before_full += earlier ? s_wave_total[wv] : 0;
+    before_tails += earlier ? s_wave_long[0][wv] : 0;
+    all_full += s_wave_total[wv];
+    all_tails += s_wave_long[0][wv];
   }
-  if (t == kPlanThreads - 1) *p.n_items = before + incl;
+  int at_full = before_full + incl_full - full;
+  int at_tail = all_full + before_tails + incl_tails - tails;
+  auto list_unit = [&](int u, int c) {
+    const int nf = c / T;
+    for (int kk = 0; kk < nf; ++kk) p.item_list[at_full + kk] = (static_cast<uint32_t>(u) << kItemBits) | kk;
+    at_full += nf;
+    if (nf * T < c) p.item_list[at_tail++] = (static_cast<uint32_t>(u) << kItemBits) | nf;
+    p.unit_items[u] = (c + T - 1) / T;
+  };
+#pragma unroll
+  for (int j = 0; j < kPlanRegUnits; ++j)
+    if (u0 + j < u1) list_unit(u0 + j, cnt[j]);
+  for (int u = u0 + kPlanRegUnits; u < u1; ++u) list_unit(u, p.unit_items[u]);
+  if (t == 0) {
+    p.n_items[0] = all_full + all_tails;
+    p.n_items[1] = T;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Listed grid: persistent waves striding over the compact item list.
+// Listed grid: persistent waves striding over the compact item list (full-
+// length items first, so each stride of the grid takes items of about one
+// length).
 // ---------------------------------------------------------------------------
 template <bool kBf16, int D>
 __global__ __launch_bounds__(64 * kWavesPerGroup) __attribute__((amdgpu_waves_per_eu(Geo<kBf16, D>::kListedWavesPerEU)))
 void split_listed_kernel(const SplitParams p) {
-  __shared__ int s_tiles[kWavesPerGroup][kMaxTilesPerItem];
+  __shared__ int s_tiles[kWavesPerGroup][kLongTiles];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int stride = gridDim.x * kWavesPerGroup;
-  const int n_items = *p.n_items;
+  const int n_items = p.n_items[0];
+  const int T = p.n_items[1];  // the item length the plan kernel chose
   int i = blockIdx.x * kWavesPerGroup + wave;
   uint32_t it_next = i < n_items ? p.item_list[i] : 0u;
   for (; i < n_items; i += stride) {
@@ -737,7 +812,8 @@ void split_listed_kernel(const SplitParams p) {
     uint32_t word = 0u;
     int incl = 0;
     const int count = sparse ? support_scan(raw, nb, lane, word, incl) : nb;
-    run_item<kBf16, D, false>(p, u, r, h, k, n, sparse, count, word, incl, lane, s_tiles[wave], p.tiles_per_item);
+    run_item<kBf16, D, false>(p, u, r, h, k, n, sparse, count, word, incl, lane, s_tiles[wave], T, nullptr,
+                              T > 8);
   }
 }
 

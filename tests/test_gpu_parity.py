@@ -183,8 +183,9 @@ def test_long_items(torch, rows, heads, tiles, dtype, d):
     """Calls with no sparse rows whose launch stays large run 16- or 32-tile
     items on the static grid (a quarter or half of the partials); sampled rows
     of every depth -- dense, discover, union, and the sparse depth on the
-    listed grid's 8-tile items -- against the oracle.  The same dense rows in
-    a call with a per-row mode array (8-tile items) agree to fp32 rounding."""
+    listed grid -- against the oracle.  The same dense rows in a call with a
+    per-row mode array (the listed grid, whose plan kernel picks the item
+    length from the same tiles) are bitwise the dense call's."""
     w = synth.Workload(name=f"long{tiles}_{rows}x{heads}_{dtype}{d}", rows=rows, heads=heads, head_dim=d, dtype=dtype,
                        page_size=16, shuffle=True, alpha=2.5, seed=93, ctx=4096, hot=6,
                        schedule=(W.WISE_DENSE, W.WISE_DISCOVER, W.WISE_DISCOVER_UNION, W.WISE_SPARSE))
@@ -201,9 +202,49 @@ def test_long_items(torch, rows, heads, tiles, dtype, d):
     harness.call(dev, ws, W.WISE_SPARSE, st, required=1,
                  row_mode=torch.full((w.rows,), W.WISE_DENSE, dtype=torch.uint8, device=dev.out.device))
     torch.cuda.synchronize()
-    diff = (dev.out - long_out).abs().max().item()
-    say(f"   long vs 8-tile items: max |diff| {diff:.2e}")
-    assert diff <= 1e-5 * max(1.0, long_out.abs().max().item())
+    assert torch.equal(dev.out, long_out)
+
+
+@pytest.mark.parametrize("rows,heads,ctx,tiles", [(64, 16, 4096, 32), (32, 16, 4096, 16), (8, 16, 4096, 8),
+                                                  (16, 16, 8192, 16)])
+def test_listed_long_items(torch, rows, heads, ctx, tiles):
+    """Calls with sparse rows take their item length in the plan kernel from
+    the tiles they attend, by the rule dense calls take on the host: 32 tiles
+    when the launch keeps at least 4096 items of 32, else 16 on that
+    condition, else 8.  With every block selected the attended tiles are the
+    causal ones, so an all-blocks sparse call and a mixed call of dense and
+    all-blocks sparse rows are bitwise the dense call; over the supports of a
+    discovery depth (near dense) sampled rows of a sparse and of a mixed call
+    match the oracle."""
+    units, nb = rows * heads, ctx // 32
+    assert tiles == (32 if units * (nb // 32) >= 4096 else 16 if units * (nb // 16) >= 4096 else 8)
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=rows, heads=heads, ctx=ctx,
+                            name=f"listed_long{tiles}_{rows}x{ctx}")
+    say(f"[{w.name}] dense vs all-blocks sparse and mixed calls; sparse and mixed vs the oracle")
+    li0, dev0 = _one_layer(w, 0)
+    li2, dev2 = _one_layer(w, 2)
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    harness.call(dev2, ws, W.WISE_DENSE)
+    torch.cuda.synchronize()
+    dense = dev2.out.clone()
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    harness.call(dev0, ws, W.WISE_DISCOVER, st, required=1)
+    torch.cuda.synchronize()
+    discovered = st.support.clone()
+    st.support.fill_(-1)  # every bit set
+    harness.call(dev2, ws, W.WISE_SPARSE, st, required=1)
+    torch.cuda.synchronize()
+    assert torch.equal(dev2.out, dense)
+    modes = np.array([W.WISE_DENSE, W.WISE_SPARSE] * (rows // 2), dtype=np.uint8)
+    harness.call(dev2, ws, W.WISE_SPARSE, st, required=1, row_mode=torch.from_numpy(modes).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(dev2.out, dense)
+    assert int(st.counters[W.CTR_FALLBACKS].item()) == 0
+    st.support.copy_(discovered)
+    sample = [0, rows // 2 + 1, rows - 1]
+    for row_modes in (None, modes):
+        rep = check_call(w, li2, dev2, ws, st, mode=W.WISE_SPARSE, row_modes=row_modes, rows=sample, required=1)
+        say(f"   {'mixed' if row_modes is not None else 'sparse'}: max_abs {rep.max_abs:.2e}")
 
 
 def test_page_size_and_layout_invariance(torch):
