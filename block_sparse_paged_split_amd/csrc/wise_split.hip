@@ -235,7 +235,8 @@ __device__ __forceinline__ RowPlan plan_row(const SplitParams &p, int r, int h =
         rp.eff = WISE_DENSE;
         rp.fallback = true;
       }
-      if (rp.req == WISE_SPARSE) rp.word = word;
+      // a sparse row attends the word's blocks; a union row ORs its selection into it
+      if (rp.req == WISE_SPARSE || rp.req == WISE_DISCOVER_UNION) rp.word = word;
     }
   }
   return rp;
@@ -547,47 +548,60 @@ __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan
   if (discover)
     for (int w = lane; w < kMaxWords; w += 64) s_bits[w] = 0u;
   sel::wave_lds_sync();
+  constexpr int kOut = D / 64;  // output elements per lane
+  float o[kOut];
   if constexpr (!kKOnly) {
-    for (int dd = lane; dd < D; dd += 64) {
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int dd = lane + 64 * i;
       float a = 0.0f;
       for (int t = 0; t < items; ++t) a = fmaf(s_acc[t * D + dd], s_w[t], a);
-      p.out[static_cast<int64_t>(u) * D + dd] = err ? __builtin_nanf("") : a / L;
+      o[i] = err ? __builtin_nanf("") : a / L;
     }
   }
-  if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
-  if (!stateful) return;
-  wise_tag *tag = p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer;
-  if (!discover) {
-    // a union row whose discovery window is broken ran dense: the rest of
-    // this token runs dense too
-    if (rp.req == WISE_DISCOVER_UNION && h == 0 && lane == 0) tag->discoveries = 0;
-    return;
-  }
+  // Selection and the new support words.  A union row ORs into the words
+  // its plan loaded (lane w holds word w; no other unit writes them).
+  const bool select = discover && !err;
   int selected = 0;
-  if (!err) {
+  uint32_t nw = 0u;
+  if (select) {
     const float2 st[1] = {lane < nb ? s_st[lane] : make_float2(0.0f, 0.0f)};
     const int K = nb <= 16   ? sel::select_eta<1, 16>(st, p.eta, nb, M, L, lane, s_bits)
                   : nb <= 32 ? sel::select_eta<1, 32>(st, p.eta, nb, M, L, lane, s_bits)
                              : sel::select_eta<1, 64>(st, p.eta, nb, M, L, lane, s_bits);
     sel::wave_lds_sync();
-    uint32_t *sw = p.support + ((static_cast<int64_t>(rp.slot) * p.layers + p.layer) * p.heads + h) * p.words;
-    int added = 0;
-    for (int w = lane; w < p.words; w += 64) {
-      const uint32_t nw = w < kMaxWords ? s_bits[w] : 0u;
-      if (rp.eff == WISE_DISCOVER) {
-        sw[w] = nw;
-      } else {
-        const uint32_t old = sw[w];
-        sw[w] = old | nw;
-        added += __popc(nw & ~old);
-      }
-    }
-    selected = rp.eff == WISE_DISCOVER ? K : sel::wave_sum_int(added);
+    nw = lane < kMaxWords ? s_bits[lane] : 0u;
+    selected = rp.eff == WISE_DISCOVER ? K : sel::wave_sum_int(__popc(nw & ~rp.word));
   }
-  if (lane != 0) return;
-  unsigned int *arrive = reinterpret_cast<unsigned int *>(&tag->reserved);
-  const unsigned int mine = 1u | (err ? 1u << 8 : 0u) | (static_cast<unsigned int>(selected) << 16);
-  const unsigned int all = atomicAdd(arrive, mine) + mine;
+  // A discovery row's arrival goes out before the stores below, which then
+  // overlap its round trip.
+  wise_tag *tag = stateful ? p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer : nullptr;
+  unsigned int *arrive = discover ? reinterpret_cast<unsigned int *>(&tag->reserved) : nullptr;
+  unsigned int all = 0u;
+  if (discover && lane == 0) {
+    const unsigned int mine = 1u | (err ? 1u << 8 : 0u) | (static_cast<unsigned int>(selected) << 16);
+    all = atomicAdd(arrive, mine) + mine;
+  }
+  if constexpr (!kKOnly) {
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) p.out[static_cast<int64_t>(u) * D + lane + 64 * i] = o[i];
+  }
+  if (select) {
+    uint32_t *sw = p.support + ((static_cast<int64_t>(rp.slot) * p.layers + p.layer) * p.heads + h) * p.words;
+    if (rp.eff == WISE_DISCOVER) {
+      for (int w = lane; w < p.words; w += 64) sw[w] = w < kMaxWords ? s_bits[w] : 0u;
+    } else if (lane < p.words && (nw & ~rp.word) != 0u) {
+      sw[lane] = rp.word | nw;  // words past kMaxWords keep their bits
+    }
+  }
+  if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
+  if (!stateful || lane != 0) return;
+  if (!discover) {
+    // a union row whose discovery window is broken ran dense: the rest of
+    // this token runs dense too
+    if (rp.req == WISE_DISCOVER_UNION && h == 0) tag->discoveries = 0;
+    return;
+  }
   if (static_cast<int>(all & 0xFFu) != p.heads) return;
   atomicExch(arrive, 0u);
   const int err_heads = static_cast<int>((all >> 8) & 0xFFu);
