@@ -247,6 +247,35 @@ def test_listed_long_items(torch, rows, heads, ctx, tiles):
         say(f"   {'mixed' if row_modes is not None else 'sparse'}: max_abs {rep.max_abs:.2e}")
 
 
+def test_plan_many_units(torch):
+    """More than 4096 units: the plan kernel's threads take five units each,
+    the fifth keeping its tile count in the workspace between the passes
+    (the first four stay in registers).  Discovery, then a sparse and a
+    mixed call (32-tile items, full-length items listed before the short
+    last ones); sampled rows against the oracle, counters exact."""
+    w = synth.Workload(name="plan_many_units", rows=260, heads=16, head_dim=64, dtype="bf16", page_size=16,
+                       shuffle=True, alpha=4.0, seed=97, ctx=1100, hot=6, schedule=(W.WISE_DISCOVER,))
+    assert w.rows * w.heads > 4 * 1024
+    say(f"[{w.name}] {w.rows * w.heads} units: discover, sparse, mixed")
+    li0, dev0 = _one_layer(w, 0)
+    li1, dev1 = _one_layer(w, 1)
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    sample = [0, 3, 77, 129, 258, 259]
+    rep = check_call(w, li0, dev0, ws, st, mode=W.WISE_DISCOVER, rows=sample, required=1)
+    say(f"   discover: max_abs {rep.max_abs:.2e} near_eta {rep.near_eta}")
+    # every plan thread's units 5t .. 5t + 4 span several rows; sampled rows cover both paths
+    rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_SPARSE, rows=sample, required=1)
+    say(f"   sparse: max_abs {rep.max_abs:.2e}")
+    modes = np.array([W.WISE_SPARSE, W.WISE_DENSE, W.WISE_SPARSE, W.WISE_DISCOVER_UNION] * (w.rows // 4),
+                     dtype=np.uint8)
+    ctr0 = st.counters.cpu().numpy().copy()
+    rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_SPARSE, row_modes=modes, rows=sample, required=1)
+    say(f"   mixed: max_abs {rep.max_abs:.2e}")
+    ctr = st.counters.cpu().numpy() - ctr0
+    assert ctr[W.CTR_FALLBACKS] == 0 and ctr[W.CTR_ERRORS] == 0
+
+
 def test_page_size_and_layout_invariance(torch):
     """Physical layout changes nothing: same bits for page sizes 8..64, a
     shuffled or identity block table, and [pages, P, H, d] storage."""
