@@ -165,6 +165,19 @@ def test_small_launches(torch, dtype, d, ctxs):
     run_schedule(w)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 128)])
+def test_maximum_context(torch, dtype, d):
+    """The longest supported context, 65536 tokens (2048 blocks: 64 support
+    words, one per lane of a plan or split wave, and the finish's widest
+    sort), beside a shorter row, through discover, union and sparse depths."""
+    w = synth.Workload(name=f"maxctx_{dtype}{d}", rows=2, heads=4, head_dim=d, dtype=dtype, page_size=16,
+                       shuffle=True, alpha=6.0, seed=101, ctx_list=(65536, 40001), hot=5,
+                       schedule=(1, 2, 3), eta=0.9)
+    assert w.max_ctx == 65536
+    reps, state = run_schedule(w)
+    assert all(r.counters[W.CTR_FALLBACKS] == 0 and r.counters[W.CTR_ERRORS] == 0 for r in reps)
+
+
 @pytest.mark.parametrize("heads,ctxs", [(1, (200, 1000)), (20, (300, 1024)), (20, (700, 3000)),
                                         (256, (64, 128))])
 def test_head_counts(torch, heads, ctxs):
