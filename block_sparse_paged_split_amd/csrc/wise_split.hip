@@ -677,8 +677,11 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanRegUnits = 4;  // units per thread whose tile counts stay in registers
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const SplitParams p) {
-  __shared__ int s_wave_total[kPlanThreads / 64];
-  __shared__ int s_wave_long[2][kPlanThreads / 64];
+  // per-wave totals; each array is written once, so no wave can overwrite
+  // a total another wave has yet to read
+  __shared__ int s_wave_long[2][kPlanThreads / 64];  // items of 32 and of 16 tiles
+  __shared__ int s_wave_full[kPlanThreads / 64];     // full-length items
+  __shared__ int s_wave_tails[kPlanThreads / 64];    // short last items
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int U = p.rows * p.heads;
@@ -763,17 +766,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const SplitParams p)
   const int incl_full = wave_inclusive_scan(full, lane);
   const int incl_tails = wave_inclusive_scan(tails, lane);
   if (lane == 63) {
-    s_wave_total[t >> 6] = incl_full;
-    s_wave_long[0][t >> 6] = incl_tails;
+    s_wave_full[t >> 6] = incl_full;
+    s_wave_tails[t >> 6] = incl_tails;
   }
   __syncthreads();
   int before_full = 0, all_full = 0, before_tails = 0, all_tails = 0;
   for (int wv = 0; wv < kPlanThreads / 64; ++wv) {
     const bool earlier = wv < (t >> 6);
-    before_full += earlier ? s_wave_total[wv] : 0;
-    before_tails += earlier ? s_wave_long[0][wv] : 0;
-    all_full += s_wave_total[wv];
-    all_tails += s_wave_long[0][wv];
+    before_full += earlier ? s_wave_full[wv] : 0;
+    before_tails += earlier ? s_wave_tails[wv] : 0;
+    all_full += s_wave_full[wv];
+    all_tails += s_wave_tails[wv];
   }
   int at_full = before_full + incl_full - full;
   int at_tail = all_full + before_tails + incl_tails - tails;
