@@ -328,6 +328,34 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
+    # ---- the same step with every call dense (no support state), replayed from
+    # HIP graphs: the step-level comparison the page makes between WISE decode and
+    # dense decode (its discovery depths cost a dense pass each; only the reuse
+    # depths can save) ----
+    dense_step_ms = None
+    if not args.no_graph and not args.no_dense_reference and not plan.mixed:
+        dgraphs = []
+        for rep in range(plan.replicas):
+            dcalls = [harness.PreparedCall(plan.kv[(rep, depth, layer % plan.kv_layers)], plan.ws, W.WISE_DENSE)
+                      for _, (_, depth, layer) in plan.calls[rep]]
+            for dc in dcalls:
+                dc.run(sh)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = int(torch.cuda.current_stream().cuda_stream)
+                for dc in dcalls:
+                    dc.run(cs)
+            dgraphs.append(g)
+        for i in range(args.warmup):
+            dgraphs[i % plan.replicas].replay()
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(args.steps):
+            dgraphs[i % plan.replicas].replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        dense_step_ms = t_start.elapsed_time(t_end) / args.steps
+
     # ---- per-mode split-kernel times and algorithmic bytes ----
     # the support a sparse call reads is the one its replica's discovery
     # depths wrote in the same step: rebuild it per replica (untimed)
@@ -476,6 +504,12 @@ def main():
             if "dense_same_kv" in modes_out:
                 entry["speedup_vs_dense"] = round(modes_out["dense_same_kv"]["split_us"] / total_us, 3)
             modes_out["page_union"] = entry
+
+    if dense_step_ms is not None:
+        modes_out["dense_step"] = {"ms_per_step": round(dense_step_ms, 4),
+                                   "wise_step_speedup": round(dense_step_ms / ms_per_step, 3),
+                                   "note": "every call of the step dense, HIP graph replay; "
+                                           "wise_step_speedup = dense step time / WISE step time"}
 
     # ---- support/tag snapshot and restore of every row's slot (KV offload and resume) ----
     if not args.no_state_copy:
