@@ -470,3 +470,47 @@ def test_graph_replay_mixed_planned_launch(torch):
         got = (d0.out, d1.out, st.support, st.tags)
         for a, b in zip(got, ref):
             assert torch.equal(a, b), f"replay {it}"
+
+
+def test_graph_replay_adapts_item_length(torch):
+    """One captured sparse call whose plan kernel picks the item length from
+    the support it finds on the device: replays over a full support (32-tile
+    items) and over a sparse one (eight-tile items), alternating, each equal
+    bit for bit to the same call run eagerly on the same state."""
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=64, heads=16, head_dim=64, ctx=4096,
+                            name="graph_item_length")
+    say(f"[{w.name}] capture one sparse call; replay over full and sparse supports")
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    dev = harness.upload(synth.layer_inputs(w, 2))
+    st.tags[:, :, 0] = st.row_request[:, None]
+    st.tags[:, :, 1] = st.row_position[:, None]
+    st.tags[:, :, 2] = 1
+    rng = np.random.default_rng(5)
+    nb = w.max_ctx // synth.BLOCK
+    sparse_bits = np.zeros((w.rows, 1, w.heads, st.words), np.uint32)
+    for r in range(w.rows):
+        for h in range(w.heads):
+            for b in rng.choice(nb, size=4, replace=False):
+                sparse_bits[r, 0, h, b // 32] |= np.uint32(1) << np.uint32(b % 32)
+    supports = {"full": torch.full_like(st.support, -1),
+                "sparse": torch.from_numpy(sparse_bits.view(np.int32)).to(st.support.device)}
+    call = harness.PreparedCall(dev, ws, W.WISE_SPARSE, st, required=1)
+    eager = {}
+    for name, sup in supports.items():
+        st.support.copy_(sup)
+        call.run(harness.stream_handle())
+        torch.cuda.synchronize()
+        eager[name] = dev.out.clone()
+    assert not torch.equal(eager["full"], eager["sparse"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.run(int(torch.cuda.current_stream().cuda_stream))
+    for it, name in enumerate(["sparse", "full", "sparse", "full"]):
+        st.support.copy_(supports[name])
+        dev.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dev.out, eager[name]), f"replay {it} ({name} support)"
+    assert int(st.counters[W.CTR_FALLBACKS].item()) == 0 and int(st.counters[W.CTR_ERRORS].item()) == 0
