@@ -164,16 +164,16 @@ __device__ __forceinline__ void bitonic_sort(unsigned long long (&key)[KPL], int
   if constexpr (SIZE < NPOS) bitonic_sort<KPL, 2 * SIZE, NPOS>(key, lane);
 }
 
-// Eta selection of one discovery unit.  st[j] holds the tile stats (m_b,
-// l_b) of block b = lane*KPL + j.  Keys (mass bits, ~b) are sorted descending over
-// NPOS positions (NPOS >= nb, a power of two; positions beyond it belong to
-// independent copies of the network holding only padding), the fp64 running
-// sum picks K, and the selected blocks' bits are ORed into s_bits.
+// Sorted keys and the cut of one discovery unit.  st[j] holds the tile
+// stats (m_b, l_b) of block b = lane*KPL + j.  Keys (mass bits, ~b) are
+// sorted descending over NPOS positions (NPOS >= nb, a power of two;
+// positions beyond it belong to independent copies of the network holding
+// only padding, which sorts after every block), and the fp64 running sum
+// picks K: the blocks of sorted positions [0, K) are selected.
 template <int KPL, int NPOS>
-__device__ __forceinline__ int select_eta(const float2 (&st)[KPL], float eta, int nb, float M, float L, int lane,
-                                          uint32_t *s_bits) {
+__device__ __forceinline__ int eta_sorted_cut(const float2 (&st)[KPL], float eta, int nb, float M, float L, int lane,
+                                              unsigned long long (&key)[KPL]) {
   const float invL = 1.0f / L;
-  unsigned long long key[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int b = lane * KPL + j;
@@ -199,7 +199,16 @@ __device__ __forceinline__ int select_eta(const float2 (&st)[KPL], float eta, in
     }
   }
   const unsigned long long hits = __builtin_amdgcn_ballot_w64(hit);
-  const int K = min(nb, hits ? __builtin_amdgcn_readlane(kfound, __builtin_ctzll(hits)) : nb);
+  return min(nb, hits ? __builtin_amdgcn_readlane(kfound, __builtin_ctzll(hits)) : nb);
+}
+
+// Eta selection of one discovery unit: the selected blocks' bits are ORed
+// into s_bits (LDS); returns K.
+template <int KPL, int NPOS>
+__device__ __forceinline__ int select_eta(const float2 (&st)[KPL], float eta, int nb, float M, float L, int lane,
+                                          uint32_t *s_bits) {
+  unsigned long long key[KPL];
+  const int K = eta_sorted_cut<KPL, NPOS>(st, eta, nb, M, L, lane, key);
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     if (lane * KPL + j < K) {
@@ -207,6 +216,24 @@ __device__ __forceinline__ int select_eta(const float2 (&st)[KPL], float eta, in
       atomicOr(&s_bits[b >> 5], 1u << (b & 31));
     }
   }
+  return K;
+}
+
+// Eta selection of a unit of at most 64 blocks, one per lane (st = the
+// stats of block `lane`): the selected set comes back as a 64-bit block
+// mask.  Sorted position p < nb holds block b_p, a permutation of [0, nb),
+// and sends lane b_p whether p < K (one forward lane permute; positions of
+// padding send to their own lanes, which hold no block).  Every lane of the
+// wave must be active.  Returns K.
+template <int NPOS>
+__device__ __forceinline__ int select_eta_mask(float2 st, float eta, int nb, float M, float L, int lane,
+                                               unsigned long long &mask) {
+  const float2 st1[1] = {st};
+  unsigned long long key[1];
+  const int K = eta_sorted_cut<1, NPOS>(st1, eta, nb, M, L, lane, key);
+  const int b = lane < nb ? static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key[0])) : lane;
+  const int picked = __builtin_amdgcn_ds_permute(b << 2, lane < K ? 1 : 0);
+  mask = __builtin_amdgcn_ballot_w64(picked != 0 && lane < nb);
   return K;
 }
 

@@ -520,7 +520,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
 template <int D, bool kKOnly>
 __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan &rp, int u, int h, int nb,
                                              int items, const float *s_acc, const float2 *s_ml,
-                                             const float2 *s_st, float *s_w, uint32_t *s_bits, int lane) {
+                                             const float2 *s_st, float *s_w, int lane) {
   const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
   const bool discover = stateful && (rp.eff == WISE_DISCOVER || rp.eff == WISE_DISCOVER_UNION);
   if constexpr (kKOnly) {
@@ -550,8 +550,6 @@ __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan
     }
     L = sel::wave_sum(Lp);
   }
-  if (discover)
-    for (int w = lane; w < kMaxWords; w += 64) s_bits[w] = 0u;
   sel::wave_lds_sync();
   constexpr int kOut = D / 64;  // output elements per lane
   float o[kOut];
@@ -564,18 +562,19 @@ __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan
       o[i] = err ? __builtin_nanf("") : a / L;
     }
   }
-  // Selection and the new support words.  A union row ORs into the words
-  // its plan loaded (lane w holds word w; no other unit writes them).
+  // Selection and the new support words (lane w holds word w; a unit has at
+  // most 64 blocks, so two words).  A union row ORs into the words its plan
+  // loaded (no other unit writes them).
   const bool select = discover && !err;
   int selected = 0;
   uint32_t nw = 0u;
   if (select) {
-    const float2 st[1] = {lane < nb ? s_st[lane] : make_float2(0.0f, 0.0f)};
-    const int K = nb <= 16   ? sel::select_eta<1, 16>(st, p.eta, nb, M, L, lane, s_bits)
-                  : nb <= 32 ? sel::select_eta<1, 32>(st, p.eta, nb, M, L, lane, s_bits)
-                             : sel::select_eta<1, 64>(st, p.eta, nb, M, L, lane, s_bits);
-    sel::wave_lds_sync();
-    nw = lane < kMaxWords ? s_bits[lane] : 0u;
+    const float2 st = lane < nb ? s_st[lane] : make_float2(0.0f, 0.0f);
+    unsigned long long mask = 0ull;
+    const int K = nb <= 16   ? sel::select_eta_mask<16>(st, p.eta, nb, M, L, lane, mask)
+                  : nb <= 32 ? sel::select_eta_mask<32>(st, p.eta, nb, M, L, lane, mask)
+                             : sel::select_eta_mask<64>(st, p.eta, nb, M, L, lane, mask);
+    nw = lane == 0 ? static_cast<uint32_t>(mask) : lane == 1 ? static_cast<uint32_t>(mask >> 32) : 0u;
     selected = rp.eff == WISE_DISCOVER ? K : sel::wave_sum_int(__popc(nw & ~rp.word));
   }
   // A discovery row's arrival goes out before the stores below, which then
@@ -594,9 +593,9 @@ __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan
   if (select) {
     uint32_t *sw = p.support + ((static_cast<int64_t>(rp.slot) * p.layers + p.layer) * p.heads + h) * p.words;
     if (rp.eff == WISE_DISCOVER) {
-      for (int w = lane; w < p.words; w += 64) sw[w] = w < kMaxWords ? s_bits[w] : 0u;
+      for (int w = lane; w < p.words; w += 64) sw[w] = w == lane ? nw : 0u;
     } else if (lane < p.words && (nw & ~rp.word) != 0u) {
-      sw[lane] = rp.word | nw;  // words past kMaxWords keep their bits
+      sw[lane] = rp.word | nw;  // the other words keep their bits
     }
   }
   if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
@@ -633,7 +632,6 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   __shared__ float2 s_ml[W];
   __shared__ float2 s_st[W * kMaxTilesPerItem];
   __shared__ float s_w[W];
-  __shared__ uint32_t s_bits[kMaxWords];
   const int lane = threadIdx.x & 63;
   const int k = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);  // item slot
   const int u = blockIdx.x;  // unit = (row, head); units of a row spread over the XCDs
@@ -658,7 +656,7 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   if (k < items)
     run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], T, &lds);
   __syncthreads();  // every wave of the workgroup reaches this once
-  if (k == 0) finish_fused<D, kKOnly>(p, rp, u, h, nb, items, s_acc, s_ml, s_st, s_w, s_bits, lane);
+  if (k == 0) finish_fused<D, kKOnly>(p, rp, u, h, nb, items, s_acc, s_ml, s_st, s_w, lane);
 }
 
 // ---------------------------------------------------------------------------
