@@ -1,13 +1,13 @@
 // Finish kernel: split merge, eta selection, union, support bookkeeping.
 //
-// WISE pull request page (vllm-rlt pull 143): "What changes" -- a finish
-// kernel merges the splits and runs the selection for discovery rows; the
-// support bitmask is [slot, layer, head, block] and tagged with (request,
-// position); "Summary" -- B = 32 blocks and the eta = 0.95 cumulative-mass
-// rule; review thread and the author's reply -- a union depth ORs its
-// selection into the previous support, and the density count adds, for the
-// first discovery depth, its selection and the causal blocks, and for a
-// union depth only the newly set blocks.
+// Method: WISE pull request page (vllm-rlt pull 143).  "What changes": a
+// second kernel combines the split partials and picks the support of the
+// discovery rows; the support is a bitmask indexed by (slot, layer, head,
+// block) and carries the request and position it was found for.
+// "Summary": 32-token blocks and a cumulative-mass target eta of 0.95.  The
+// review thread and the author's reply on density: a union depth ORs its
+// pick into the earlier one, and the density count takes the first depth's
+// pick and causal blocks, then only the bits a union depth newly sets.
 //
 // One workgroup per row for units of up to 64 blocks (a row with more than
 // 16 heads takes several), one per 4 heads for longer units; one wave64 per

@@ -1,9 +1,10 @@
 // Head-union, page-granular support through a compacted page table.
 //
-// WISE pull request page (vllm-rlt pull 143), "What changes", second bullet:
-// on the FlashAttention route a sparse row attends the union over its heads
-// of the layer's support, at page granularity, through a compacted page
-// table; "Limits": pages of 256 tokens or more make that union nearly dense.
+// Method: WISE pull request page (vllm-rlt pull 143), "What changes", second
+// bullet (the FlashAttention route: each sparse row reads the whole KV pages
+// that hold a block any head of the layer picked, through a shortened page
+// table) and "Limits" (with pages of 256 tokens or more, that union leaves
+// almost nothing out).
 //
 // One wave64 per row:
 //  * plan as a SPARSE row (tag of the (slot, layer): same request and

@@ -1,12 +1,15 @@
 // Split-KV paged decode attention with per-row modes (dense / discover /
 // discover-union / sparse) for gfx950.
 //
-// WISE pull request page (vllm-rlt pull 143), "What changes": one split-KV
-// paged decode kernel with per-row modes -- dense; discover = dense while
-// recording each 32-token tile's max and sum; sparse = only the row's
-// selected tiles, compacted first so the loop has no branch -- whose
-// programs each cover about eight tiles, so a long dense row does not set
-// the latency of a launch whose other rows are sparse.
+// Method: WISE pull request page (vllm-rlt pull 143), "What changes", first
+// bullet (the split kernel's row modes, its finish step and the size of its
+// programs).  Restated: a discovery row is attended in full and leaves, per
+// 32-token tile, the max and the exp-sum of its scores; a sparse row visits
+// only the tiles of its support, whose indices are gathered into a dense
+// list before the tile loop so that the loop body has no per-tile test; and
+// work items stay near eight tiles, so that in a launch mixing long dense
+// rows with short sparse ones the longest row does not decide when the
+// launch ends.
 //
 // MI355X design:
 //  * One wave64 per work item (<= tiles_per_item consecutive entries of a

@@ -1,13 +1,13 @@
 // Support/tag snapshot and restore across a KV offload.
 //
-// WISE pull request page (vllm-rlt pull 143), review finding "Preserve WISE
-// state across KV offload": freeing a request for capacity offload after its
-// discovery depths deletes its support slot and tags, so a request resumed
-// at a reuse depth has no discovery for its token; the finding asks for the
-// support and tags to be snapshotted and restored alongside the recurrent
-// state.  These kernels copy whole slots (every layer and head) between the
-// support state and caller-owned records, so the resumed request's tag again
-// names its (request, position) and reuse proceeds sparse.
+// Method: WISE pull request page (vllm-rlt pull 143), review finding
+// "Preserve WISE state across KV offload".  Restated: an offload after the
+// discovery depths drops the request's slot, so its later reuse depths find
+// no support for their token; the finding proposes saving the support and
+// tags with the recurrent state and putting them back on resume.  These
+// kernels copy whole slots (every layer and head) between the support state
+// and caller-owned records; a restored tag names the same (request,
+// position), so the resumed request reuses sparsely.
 //
 // Record layout (one per listed slot, record_bytes apart, 8-byte aligned):
 //   support words [layers][heads][words] uint32, padded to 8 bytes,

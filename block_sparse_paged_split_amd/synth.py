@@ -100,6 +100,9 @@ class Workload:
     # reuse depths read a random support of this density set directly
     # (no discovery), as a kernel benchmark does
     fixed_density: Optional[float] = None
+    # every key of a (row, head) is the same draw (exactly tied scores, so
+    # every full block carries the same softmax mass); no planting
+    tied_keys: bool = False
     note: str = ""
 
     @property
@@ -235,6 +238,9 @@ def row_qkv(w: Workload, depth: int, layer: int, row: int, n: int):
     q = g.standard_normal((H, d), dtype=np.float32)
     K = g.standard_normal((H, n, d), dtype=np.float32)
     V = g.standard_normal((H, n, d), dtype=np.float32)
+    if w.tied_keys:
+        K[:] = K[:, :1]
+        return q, K, V
     nb = (n + BLOCK - 1) // BLOCK
     hb = hot_blocks(w, layer, row, nb)
     for h in range(H):
@@ -311,8 +317,10 @@ def _fill_row(w: Workload, depth: int, layer: int, r: int, n: int, bt_row, q, k,
     g.standard_normal(out=K, dtype=np.float32)
     g.standard_normal(out=V, dtype=np.float32)
     nb = (n + BLOCK - 1) // BLOCK
-    hb = hot_blocks(w, layer, r, nb)
-    for h in range(H):
+    hb = [] if w.tied_keys else hot_blocks(w, layer, r, nb)
+    if w.tied_keys:
+        K[:] = K[:, :1]
+    for h in range(len(hb)):
         off = np.float32(w.alpha) * (qf[h] / np.float32(np.linalg.norm(qf[h])))
         for b in hb[h]:
             K[h, b * BLOCK: min(b * BLOCK + BLOCK, n)] += off

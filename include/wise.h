@@ -163,23 +163,33 @@ typedef struct wise_support {
   uint64_t *counters;
 } wise_support;
 
-/* Bytes of workspace a call with these sizes needs (0 if unsupported). */
+/* Bytes of workspace a call with these sizes needs (0 if unsupported).
+ * The workspace holds the split partials and tile statistics the finish
+ * step merges ("What changes", first bullet: the split kernel's partials
+ * and a finish step over them). */
 size_t wise_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t max_ctx);
 
-/* Every row DENSE.  No support state is read or written.  Follow with
- * wise_finish_select(a, NULL, ...). */
+/* Every row DENSE ("What changes", first bullet: the dense row mode of the
+ * split-KV paged decode).  No support state is read or written.  Follow
+ * with wise_finish_select(a, NULL, ...). */
 wise_status wise_decode_dense(const wise_attn *a, void *ws, size_t ws_bytes, void *stream);
 
-/* Every row DISCOVER (union_with_previous == 0) or DISCOVER_UNION (!= 0):
- * dense attention that also records every tile's (max, sum).  Follow with
- * wise_finish_select(a, s, ...), which selects and updates the state. */
+/* Every row DISCOVER (union_with_previous == 0) or DISCOVER_UNION (!= 0)
+ * ("What changes", first bullet: the discover row mode; "Summary": the
+ * discovery depths; review thread and the author's reply: the second
+ * discovery depth ORs into the first): dense attention that also records
+ * every tile's (max, sum).  Follow with wise_finish_select(a, s, ...), which
+ * selects and updates the state. */
 wise_status wise_decode_discover(const wise_attn *a, const wise_support *s,
                                  int32_t union_with_previous, void *ws, size_t ws_bytes,
                                  void *stream);
 
 /* Every row SPARSE (row_mode == NULL), or per-row modes from the device
  * array row_mode [rows] uint8 (one launch mixes dense, discover, union and
- * sparse rows).  Sparse rows walk only the tiles of their support, whose
+ * sparse rows) ("What changes", first bullet: the sparse row mode over a
+ * compacted tile list, and one launch of rows in different modes; third
+ * bullet: a row without a complete discovery for its token runs dense and
+ * is counted).  Sparse rows walk only the tiles of their support, whose
  * list is compacted before the loop.  Follow with wise_finish_select(a, s). */
 wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
                                const uint8_t *row_mode, void *ws, size_t ws_bytes,
@@ -187,7 +197,9 @@ wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
 
 /* Merge the splits of the preceding decode call into a->out; for discovery
  * rows run the eta selection, write/OR the support, update the tags and
- * the counters.  `a` and `s` must describe the same call as the decode
+ * the counters ("What changes", first bullet: the finish kernel; "Summary":
+ * B = 32 blocks and the eta = 0.95 rule; the author's reply on density: the
+ * selected and causal block counts).  `a` and `s` must describe the same call as the decode
  * call (s == NULL after wise_decode_dense).  When every (row, head)'s work
  * items fit one split workgroup the decode call has already done all of
  * this in the same kernel, and this call only validates its arguments:

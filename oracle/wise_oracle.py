@@ -7,20 +7,19 @@ library and does not import it; it reads only the raw arrays produced by
 the seeded input generator (bf16 bit patterns are widened exactly).
 
 Source: the WISE pull request page (InferMatrixLab/vllm-rlt pull 143).
-Its "Summary" names the method (find each query's attention support in the
-early recurrent loops with B = 32 blocks and an eta = 0.95 cumulative-mass
-rule; later loops attend only that support, with Q/K/V still dynamic).  Its
-"What changes" section fixes the kernel steps: dense decode, discover =
-dense while recording every 32-token tile's max and sum, sparse = only the
-selected tiles; a finish step merges splits and runs the selection; the
-support is a [slot, layer, head, block] bitmask tagged with its (request,
-position), and a token whose discovery is incomplete attends densely at its
-remaining depths, counted as a fallback.  Its "Tests" section fixes the
-checks: sparse output equals masked attention, selection matches the rule
-and the union across discovery depths.  The review thread and the author's
-replies fix the union semantics (the second discovery depth ORs into the
-first) and the density count (first discovery adds its selection and the
-causal blocks; a union depth adds only newly set blocks).
+"Summary": the early recurrent depths determine, per query, which 32-token
+blocks hold its attention (an eta = 0.95 cumulative-mass rule); the later
+depths attend those blocks only, recomputing q, K, V and the softmax inside
+them.  "What changes": a split kernel whose rows are dense, discovering
+(dense, plus each 32-token tile's score max and exp-sum) or sparse (the
+support's tiles only); a second step that merges the splits and selects for
+discovering rows; the support as a [slot, layer, head, block] bitmask tagged
+with its (request, position); a token without a complete discovery runs
+dense for the rest of its depths and is counted.  "Tests": sparse output is
+masked attention, and the selection follows the rule and the union over
+discovery depths.  Review thread and author's replies: the second discovery
+depth ORs into the first; the density count takes the first depth's pick
+and causal blocks, then only the bits a union depth newly sets.
 
 Where the page is silent, this oracle takes these readings:
   * softmax scale defaults to 1/sqrt(head_dim);

@@ -1,6 +1,8 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
-times: every row runs on the GPU, sampled rows are checked one by one
-against the fp64 oracle (outputs, supports, tags, tile masses).
+times: every row runs on the GPU and every row is checked against the fp64
+oracle (outputs, supports, tags, tile masses, counters), the oracle running
+in worker processes; the eta sweep's outer values and the LSE route check
+sampled rows.
 """
 
 import dataclasses
@@ -28,10 +30,9 @@ def torch():
 
 
 def test_ctx4k_24_layers(torch):
-    """64 rows at 4K, 24 layers per depth: layers 0 and 23 of the 4-depth
-    schedule, each against its own support slice."""
+    """64 rows at 4K, 24 layers per depth: every row of layers 0 and 23 of the
+    4-depth schedule, each against its own support slice."""
     w = synth.WORKLOADS["ctx4k_24l"]
-    rows = [0, 21, 42, 63]
     state = harness.SupportState(w.rows, w.heads, w.max_ctx, layers=w.layers)
     state.row_position.fill_(3)
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
@@ -40,7 +41,7 @@ def test_ctx4k_24_layers(torch):
             say(f"[ctx4k_24l] layer {layer} depth {depth} mode {mode}")
             li = synth.layer_inputs(w, depth, layer)
             dev = harness.upload(li, with_stats=True)
-            rep = check_call(w, li, dev, ws, state, mode=mode, layer=layer, rows=rows)
+            rep = check_call(w, li, dev, ws, state, mode=mode, layer=layer, pool=True)
             say(f"   max_abs {rep.max_abs:.2e} near_eta {rep.near_eta} near_tie {rep.near_tie} "
                 f"mismatch {rep.support_mismatch} counters {rep.counters}")
             assert rep.counters[W.CTR_FALLBACKS] == 0 and rep.counters[W.CTR_ERRORS] == 0
@@ -63,17 +64,12 @@ def test_ctx8k_mixed_launch(torch):
     # that are not flagged complete their window with a union at depth 1
     d0 = np.where(modes == W.WISE_DENSE, W.WISE_DENSE, W.WISE_DISCOVER).astype(np.uint8)
     d1 = np.where((modes == W.WISE_SPARSE) & ~flagged, W.WISE_DISCOVER_UNION, W.WISE_DENSE).astype(np.uint8)
-    pick = []
-    for m in (W.WISE_DENSE, W.WISE_DISCOVER, W.WISE_DISCOVER_UNION, W.WISE_SPARSE):
-        pick += [int(r) for r in np.nonzero((modes == m) & ~flagged)[0][:2]]
-    pick += [int(r) for r in np.nonzero(flagged)[0]]
-    pick = sorted(set(pick))
     for depth, rm in ((0, d0), (1, d1), (2, modes)):
-        say(f"[ctx8k_mixed] depth {depth} modes {np.bincount(rm, minlength=4)} rows {pick}")
+        say(f"[ctx8k_mixed] depth {depth} modes {np.bincount(rm, minlength=4)}, every row")
         li = synth.layer_inputs(w, depth)
         dev = harness.upload(li, with_stats=True)
         fb0 = int(state.counters[W.CTR_FALLBACKS].item())
-        rep = check_call(w, li, dev, ws, state, mode=W.WISE_SPARSE, row_modes=rm, rows=pick)
+        rep = check_call(w, li, dev, ws, state, mode=W.WISE_SPARSE, row_modes=rm, pool=True)
         say(f"   max_abs {rep.max_abs:.2e} near_eta {rep.near_eta} near_tie {rep.near_tie} "
             f"mismatch {rep.support_mismatch} counters {rep.counters}")
         fallbacks = int(state.counters[W.CTR_FALLBACKS].item()) - fb0
@@ -83,8 +79,9 @@ def test_ctx8k_mixed_launch(torch):
 
 def test_ragged_eta_sweep(torch):
     """128 rows, contexts log-uniform over 512..32768, 1-16 planted blocks;
-    the schedule at eta 0.9, 0.95 and 0.99 on identical data.  Supports of
-    one depth are nested across eta."""
+    the schedule at eta 0.9, 0.95 and 0.99 on identical data: every row at
+    eta 0.95, sampled rows at 0.9 and 0.99.  Supports of one depth are nested
+    across eta."""
     w = synth.WORKLOADS["ragged"]
     ctx = synth.context_lengths(w)
     order = np.argsort(ctx)
@@ -104,7 +101,11 @@ def test_ragged_eta_sweep(torch):
         state = harness.SupportState(w.rows, w.heads, w.max_ctx)
         for depth, mode in enumerate(w.schedule):
             say(f"[ragged] eta {eta} depth {depth} mode {mode}")
-            rep = check_call(w, samples[depth], devs[depth], ws, state, mode=mode, rows=rows, eta=eta)
+            if eta == 0.95:
+                # every row: the oracle's workers regenerate the rows they evaluate
+                rep = check_call(w, samples[depth], devs[depth], ws, state, mode=mode, eta=eta, pool=True)
+            else:
+                rep = check_call(w, samples[depth], devs[depth], ws, state, mode=mode, rows=rows, eta=eta)
             say(f"   max_abs {rep.max_abs:.2e} near_eta {rep.near_eta} near_tie {rep.near_tie} "
                 f"mismatch {rep.support_mismatch} counters {rep.counters}")
             if depth == 0:

@@ -29,8 +29,9 @@ def torch():
     return t
 
 
-def run_schedule(w, rows=None, layer=0, eta=None, required=None, with_stats=True):
-    """All depths of w.schedule for one layer, each checked against the oracle."""
+def run_schedule(w, rows=None, layer=0, eta=None, required=None, with_stats=True, pool=False):
+    """All depths of w.schedule for one layer, each checked against the oracle
+    (in worker processes with ``pool``)."""
     state = harness.SupportState(w.rows, w.heads, w.max_ctx, layers=max(w.layers, layer + 1))
     state.row_position.fill_(17)
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
@@ -40,7 +41,7 @@ def run_schedule(w, rows=None, layer=0, eta=None, required=None, with_stats=True
         li = synth.layer_inputs(w, depth, layer)
         dev = harness.upload(li, with_stats=with_stats)
         reps.append(check_call(w, li, dev, ws, state, mode=mode, layer=layer, rows=rows,
-                               eta=eta, required=required))
+                               eta=eta, required=required, pool=pool))
         say(f"   max_abs {reps[-1].max_abs:.2e} near_eta {reps[-1].near_eta} "
             f"near_tie {reps[-1].near_tie} counters {reps[-1].counters}")
     return reps, state
@@ -204,7 +205,7 @@ def test_long_items(torch, rows, heads, tiles, dtype, d):
                        schedule=(W.WISE_DENSE, W.WISE_DISCOVER, W.WISE_DISCOVER_UNION, W.WISE_SPARSE))
     units = rows * heads
     assert units * (128 // tiles) >= 4096 and (tiles == 32 or units * (128 // 32) < 4096)
-    reps, state = run_schedule(w, rows=[0, 7, rows - 1])
+    reps, state = run_schedule(w, pool=True)
     assert all(r.counters[W.CTR_FALLBACKS] == 0 and r.counters[W.CTR_ERRORS] == 0 for r in reps)
     li, dev = _one_layer(w, 0)
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
@@ -227,8 +228,8 @@ def test_listed_long_items(torch, rows, heads, ctx, tiles):
     condition, else 8.  With every block selected the attended tiles are the
     causal ones, so an all-blocks sparse call and a mixed call of dense and
     all-blocks sparse rows are bitwise the dense call; over the supports of a
-    discovery depth (near dense) sampled rows of a sparse and of a mixed call
-    match the oracle."""
+    discovery depth (near dense) every row of a sparse and of a mixed call
+    matches the oracle."""
     units, nb = rows * heads, ctx // 32
     assert tiles == (32 if units * (nb // 32) >= 4096 else 16 if units * (nb // 16) >= 4096 else 8)
     w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=rows, heads=heads, ctx=ctx,
@@ -254,9 +255,8 @@ def test_listed_long_items(torch, rows, heads, ctx, tiles):
     assert torch.equal(dev2.out, dense)
     assert int(st.counters[W.CTR_FALLBACKS].item()) == 0
     st.support.copy_(discovered)
-    sample = [0, rows // 2 + 1, rows - 1]
     for row_modes in (None, modes):
-        rep = check_call(w, li2, dev2, ws, st, mode=W.WISE_SPARSE, row_modes=row_modes, rows=sample, required=1)
+        rep = check_call(w, li2, dev2, ws, st, mode=W.WISE_SPARSE, row_modes=row_modes, required=1, pool=True)
         say(f"   {'mixed' if row_modes is not None else 'sparse'}: max_abs {rep.max_abs:.2e}")
 
 
@@ -265,7 +265,7 @@ def test_plan_many_units(torch):
     the fifth keeping its tile count in the workspace between the passes
     (the first four stay in registers).  Discovery, then a sparse and a
     mixed call (32-tile items, full-length items listed before the short
-    last ones); sampled rows against the oracle, counters exact."""
+    last ones); every row against the oracle, counters exact."""
     w = synth.Workload(name="plan_many_units", rows=260, heads=16, head_dim=64, dtype="bf16", page_size=16,
                        shuffle=True, alpha=4.0, seed=97, ctx=1100, hot=6, schedule=(W.WISE_DISCOVER,))
     assert w.rows * w.heads > 4 * 1024
@@ -274,16 +274,15 @@ def test_plan_many_units(torch):
     li1, dev1 = _one_layer(w, 1)
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
     st = harness.SupportState(w.rows, w.heads, w.max_ctx)
-    sample = [0, 3, 77, 129, 258, 259]
-    rep = check_call(w, li0, dev0, ws, st, mode=W.WISE_DISCOVER, rows=sample, required=1)
+    rep = check_call(w, li0, dev0, ws, st, mode=W.WISE_DISCOVER, required=1, pool=True)
     say(f"   discover: max_abs {rep.max_abs:.2e} near_eta {rep.near_eta}")
-    # every plan thread's units 5t .. 5t + 4 span several rows; sampled rows cover both paths
-    rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_SPARSE, rows=sample, required=1)
+    # every plan thread's units 5t .. 5t + 4 span several rows
+    rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_SPARSE, required=1, pool=True)
     say(f"   sparse: max_abs {rep.max_abs:.2e}")
     modes = np.array([W.WISE_SPARSE, W.WISE_DENSE, W.WISE_SPARSE, W.WISE_DISCOVER_UNION] * (w.rows // 4),
                      dtype=np.uint8)
     ctr0 = st.counters.cpu().numpy().copy()
-    rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_SPARSE, row_modes=modes, rows=sample, required=1)
+    rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_SPARSE, row_modes=modes, required=1, pool=True)
     say(f"   mixed: max_abs {rep.max_abs:.2e}")
     ctr = st.counters.cpu().numpy() - ctr0
     assert ctr[W.CTR_FALLBACKS] == 0 and ctr[W.CTR_ERRORS] == 0
@@ -515,3 +514,102 @@ def test_graph_replay_adapts_item_length(torch):
         torch.cuda.synchronize()
         assert torch.equal(dev.out, eager[name]), f"replay {it} ({name} support)"
     assert int(st.counters[W.CTR_FALLBACKS].item()) == 0 and int(st.counters[W.CTR_ERRORS].item()) == 0
+
+
+def _oracle_chain_check(w, lis, devs, st, schedule, row_modes, required):
+    """Check the results of one replayed step against the oracle run depth by
+    depth from an empty state: outputs of every depth, the support after the
+    discovery depths (exact but for the excused classes), tags and counters.
+    Reuse depths are evaluated over the support the GPU holds, as in
+    ``check_call``."""
+    from parity import Report, assert_close, check_unit_support
+    R, H = w.rows, w.heads
+    words = st.words
+    sup = np.zeros((R, 1, H, words), np.uint32)
+    tags = np.zeros((R, 1), O.TAG_DTYPE)
+    gpu_sup = st.support_numpy()
+    rep = Report()
+    counters = np.zeros(4, np.int64)
+    for depth, (li, dev) in enumerate(zip(lis, devs)):
+        modes = row_modes[depth] if row_modes[depth] is not None else np.full(R, schedule[depth])
+        reuse = all(int(m) in (W.WISE_SPARSE, W.WISE_DENSE) for m in modes)
+        ref = O.run_call(q=li.q, k_cache=li.k, v_cache=li.v, block_table=li.block_table, ctx_len=li.ctx_len,
+                         page_size=w.page_size, num_pages=li.num_pages, max_ctx=w.max_ctx, modes=modes,
+                         support=gpu_sup if reuse else sup, tags=tags, row_request=st.row_request.cpu().numpy(),
+                         row_position=st.row_position.cpu().numpy(), required=required, eta=w.eta)
+        out = dev.out.cpu().numpy()
+        for r in range(R):
+            assert_close(out[r], ref.out[r], w.dtype, f"depth {depth} row {r}", rep)
+        if not reuse:
+            for r in range(R):
+                for h in range(H):
+                    u = ref.units.get((r, h))
+                    if u is not None and u.selection is not None:
+                        rep.units += 1
+                        nb = (int(li.ctx_len[r]) + 31) // 32
+                        last = all(int(m) in (W.WISE_SPARSE, W.WISE_DENSE)
+                                   for m in (row_modes[d][r] if row_modes[d] is not None else schedule[d]
+                                             for d in range(depth + 1, len(lis))))
+                        if last:   # the GPU's support after this depth is its final one
+                            check_unit_support(gpu_sup[r, 0, h], ref.support[r, 0, h], u.selection, w.eta, nb,
+                                               sup[r, 0, h], u.effective == O.DISCOVER_UNION, rep,
+                                               f"depth {depth} row {r} head {h}")
+        sup, tags = ref.support, ref.tags
+        counters += ref.counters
+    gt = st.tags_numpy()
+    for f in ("request", "position", "discoveries"):
+        np.testing.assert_array_equal(gt[f], tags[f])
+    ctr = st.counters.cpu().numpy()
+    assert ctr[W.CTR_FALLBACKS] == counters[0] and ctr[W.CTR_ERRORS] == counters[3]
+    assert ctr[W.CTR_CAUSAL] == counters[2]
+    if rep.support_mismatch == 0:
+        assert ctr[W.CTR_SELECTED] == counters[1]
+    return rep
+
+
+@pytest.mark.parametrize("case", ["ctx1k", "mixed4k"])
+def test_graph_replay_matches_oracle(torch, case):
+    """A whole step captured in a HIP graph and replayed from an empty support
+    state, twice, each replay checked against the oracle's own schedule: the
+    ctx1k step (discover, union, sparse, sparse; the fused launch shape) and
+    a discovery depth followed by a mixed launch at 4K (the plan kernel, the
+    listed split and the finish kernel)."""
+    if case == "ctx1k":
+        w = synth.WORKLOADS["ctx1k"]
+        schedule, row_modes, required = list(w.schedule), [None] * 4, w.discoveries
+    else:
+        w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=8, ctx=4096, name="graph_mixed4k_oracle")
+        schedule = [W.WISE_DISCOVER, W.WISE_SPARSE]
+        row_modes = [None, np.array([0, 1, 2, 3, 3, 3, 2, 1], np.uint8)]
+        required = 1
+    say(f"[{w.name}] capture one step, replay x2 from an empty state, each against the oracle")
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    st.row_position.fill_(5)
+    lis = [synth.layer_inputs(w, d) for d in range(len(schedule))]
+    devs = [harness.upload(li) for li in lis]
+    rm_dev = [None if m is None else torch.from_numpy(m).cuda() for m in row_modes]
+    calls = [harness.PreparedCall(devs[d], ws, schedule[d], st, required=required, eta=w.eta, row_mode=rm_dev[d])
+             for d in range(len(schedule))]
+
+    def step(stream):
+        for c in calls:
+            c.run(stream)
+
+    step(harness.stream_handle())       # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(int(torch.cuda.current_stream().cuda_stream))
+    for it in range(2):
+        st.support.zero_()
+        st.tags.zero_()
+        st.counters.zero_()
+        for d in devs:
+            d.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rep = _oracle_chain_check(w, lis, devs, st, schedule, row_modes, required)
+        say(f"   replay {it}: max_abs {rep.max_abs:.2e} units {rep.units} class A {rep.near_eta} "
+            f"class B {rep.near_tie} mismatches {rep.support_mismatch}")

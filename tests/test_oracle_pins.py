@@ -123,6 +123,60 @@ def test_tile_stats_and_mass(n):
         assert l[b] == pytest.approx(math.fsum(math.exp(x - max(seg)) for x in seg), rel=1e-14)
 
 
+def test_tile_stats_of_subset_brute_force():
+    """Tile stats of a token subset (what a sparse unit attends): the blocks
+    are the absolute 32-token ranges the tokens fall in, not runs of 32
+    entries of the gathered list; a partial last block is a block."""
+    rng = np.random.default_rng(21)
+    n = 200                                          # blocks 0..6, block 6 holds 8 tokens
+    s_all = rng.standard_normal(n) * 3
+    for blocks in ([6], [0, 2, 6], [1, 3, 4], [5], list(range(7))):
+        toks = np.nonzero(O.token_mask(blocks, n))[0]
+        m, l = O.tile_stats_of(s_all[toks], toks)
+        assert len(m) == len(blocks)
+        for i, b in enumerate(blocks):
+            seg = [float(s_all[t]) for t in range(32 * b, min(n, 32 * b + 32))]
+            assert m[i] == max(seg)
+            assert l[i] == pytest.approx(math.fsum(math.exp(x - max(seg)) for x in seg), rel=1e-14)
+    # the whole context gives the dense tile stats, bit for bit
+    toks = np.arange(n)
+    m, l = O.tile_stats_of(s_all, toks)
+    m2, l2 = O.tile_stats(s_all)
+    np.testing.assert_array_equal(m, m2)
+    np.testing.assert_allclose(l, l2, rtol=1e-15, atol=0)
+
+
+def test_widen_bf16_bit_patterns():
+    """bf16 bits -> fp64 by the format's definition (1 sign, 8 exponent bits
+    with bias 127, 7 mantissa bits; exponent 0 is subnormal), evaluated here
+    with exact binary arithmetic, never by the oracle's own shift."""
+    def bf16_value(bits):
+        sign = -1.0 if bits >> 15 else 1.0
+        e, m = (bits >> 7) & 0xFF, bits & 0x7F
+        if e == 0:
+            return sign * math.ldexp(m, -126 - 7)
+        assert e != 0xFF
+        return sign * math.ldexp(128 + m, e - 127 - 7)
+
+    cases = {0x3F80: 1.0, 0xC020: -2.5, 0x4049: 3.140625, 0x3F81: 1.0 + 2 ** -7,
+             0x0001: 2.0 ** -133, 0x807F: -(127 * 2.0 ** -133), 0x0080: 2.0 ** -126,
+             0x7F7F: (2 - 2 ** -7) * 2.0 ** 127, 0xFF7F: -(2 - 2 ** -7) * 2.0 ** 127,
+             0x0000: 0.0, 0x8000: -0.0}
+    bits = np.array(sorted(cases), dtype=np.uint16)
+    got = O.widen(bits)
+    assert got.dtype == np.float64
+    for b, g in zip(bits.tolist(), got.tolist()):
+        assert g == cases[b] == bf16_value(b), hex(b)
+        assert math.copysign(1.0, g) == math.copysign(1.0, cases[b]), hex(b)   # -0.0 keeps its sign
+    rng = np.random.default_rng(8)
+    rnd = rng.integers(0, 0x7F80, size=500).astype(np.uint16) | (rng.integers(0, 2, 500) << 15).astype(np.uint16)
+    np.testing.assert_array_equal(O.widen(rnd), np.array([bf16_value(int(b)) for b in rnd]))
+    # fp32 input passes through exactly; shape is kept
+    x = np.array([[1.5, -2.0 ** -149], [3.0e38, 0.1]], np.float32)
+    np.testing.assert_array_equal(O.widen(x), x.astype(np.float64))
+    assert O.widen(bits.reshape(1, -1)).shape == (1, len(bits))
+
+
 # ----------------------------------------------------------------------------- O5 selection
 
 def brute_select(p, eta):
@@ -636,7 +690,35 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         return np.array(sorted({j for b in blocks for j in range(32 * b // P, (32 * b + 31) // P + 1)}),
                         dtype=np.int64)
 
+    real_widen, real_stats_of = O.widen, O.tile_stats_of
+
+    def widen_as_integers(x):                   # bf16 bit patterns taken as integer values
+        x = np.asarray(x)
+        return x.astype(np.float64)
+
+    def widen_shift15(x):                       # one bit short of the fp32 layout
+        x = np.asarray(x)
+        if x.dtype == np.uint16:
+            return (x.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+        return x.astype(np.float64)
+
+    def stats_of_row_max(s, tokens):            # every block's max taken as the subset's max
+        blk = np.asarray(tokens) // 32
+        ids = np.unique(blk)
+        mx = float(np.max(s))
+        return np.full(len(ids), mx), np.array([np.exp(s[blk == b] - mx).sum() for b in ids])
+
+    def stats_of_unclipped(s, tokens):          # sum over the block's first token only
+        blk = np.asarray(tokens) // 32
+        ids = np.unique(blk)
+        m = np.array([s[blk == b].max() for b in ids])
+        return m, np.array([np.exp(s[blk == b][:1] - mb).sum() for b, mb in zip(ids, m)])
+
     planted = [
+        ("widen", widen_as_integers, lambda: test_widen_bf16_bit_patterns()),
+        ("widen", widen_shift15, lambda: test_widen_bf16_bit_patterns()),
+        ("tile_stats_of", stats_of_row_max, lambda: test_tile_stats_of_subset_brute_force()),
+        ("tile_stats_of", stats_of_unclipped, lambda: test_tile_stats_of_subset_brute_force()),
         ("union_pages", pages_whole_block, lambda: test_union_pages_brute_force(8)),
         ("eta_select", strict_cut, lambda: test_selection_dominant_and_single_block()),
         ("eta_select", index_desc, lambda: test_selection_tie_break_equal_masses()),
@@ -646,7 +728,8 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         ("lse_block_mass", lse_full_blocks, lambda: test_lse_block_mass_closed_form()),
     ]
     reals = {"eta_select": real_select, "block_mass": real_mass, "tile_stats": real_stats,
-             "lse_block_mass": real_lse_mass, "union_pages": real_union_pages}
+             "lse_block_mass": real_lse_mass, "union_pages": real_union_pages,
+             "widen": real_widen, "tile_stats_of": real_stats_of}
     for name, fn, pin in planted:
         monkeypatch.setattr(O, name, fn)
         with pytest.raises(AssertionError):
