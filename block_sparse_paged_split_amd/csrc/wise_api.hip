@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "wise_internal.h"
 
@@ -289,6 +290,35 @@ wise_status finish(const wise_attn *a, const wise_support *s, const float *lse, 
   return WISE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The library's own workspace, for callers that cannot allocate one.
+// ---------------------------------------------------------------------------
+
+// One copy per GPU, reserved when the library's code is loaded on that GPU
+// and held until the process ends.  In host code this name is only a
+// stand-in for the symbol, never a device address: the address of the
+// current device's copy comes from hipGetSymbolAddress (once per device) and
+// is the only one host code hands to kernels.  Nothing in it needs to start
+// at zero: every call's kernels write what they later read.
+__device__ __align__(256) unsigned char scratch[WISE_SCRATCH_BYTES];
+
+std::mutex scratch_mutex;
+void *scratch_address[64] = {nullptr};
+
+// Device address of the current device's scratch copy, looked up on the
+// first call on each device; NULL if the lookup fails.
+void *device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_address[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_address[dev] = ptr;
+  }
+  return scratch_address[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -370,6 +400,21 @@ wise_status wise_compact_pages(const wise_attn *a, const wise_support *s, const 
   p.ctx_out = ctx_out;
   if (launch_compact_pages(p, static_cast<hipStream_t>(stream)) != hipSuccess) return WISE_E_HIP;
   return WISE_OK;
+}
+
+wise_status wise_decode_sparse_noalloc(const wise_attn *a, const wise_support *s, const uint8_t *row_mode,
+                                       void *stream) {
+  // every host check, the size limit included, before the device is touched
+  Layout L;
+  wise_status st = check_attn(a, &L);
+  if (st == WISE_OK) st = check_support(a, s, L);
+  if (st != WISE_OK) return st;
+  if (L.total > static_cast<size_t>(WISE_SCRATCH_BYTES)) return WISE_E_WORKSPACE;
+  void *ws = device_scratch();
+  if (ws == nullptr) return WISE_E_HIP;
+  st = decode(a, s, WISE_SPARSE, row_mode, ws, L.total, stream);
+  if (st != WISE_OK) return st;
+  return finish(a, s, nullptr, ws, L.total, stream);
 }
 
 size_t wise_snapshot_bytes(int32_t layers, int32_t heads, int32_t words) {

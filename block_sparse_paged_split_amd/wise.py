@@ -26,7 +26,9 @@ BLOCK = 32
 
 EXPORTED = ("wise_workspace_size", "wise_decode_dense", "wise_decode_discover",
             "wise_decode_sparse", "wise_finish_select", "wise_discover_lse", "wise_compact_pages",
-            "wise_snapshot_bytes", "wise_support_snapshot", "wise_support_restore", "wise_status_string")
+            "wise_snapshot_bytes", "wise_support_snapshot", "wise_support_restore", "wise_status_string",
+            "wise_decode_sparse_noalloc")
+SCRATCH_BYTES = 32 << 20  # WISE_SCRATCH_BYTES
 
 
 class WiseTag(ctypes.Structure):
@@ -86,7 +88,8 @@ def lib() -> ctypes.CDLL:
         L.wise_snapshot_bytes.argtypes = [ctypes.c_int32] * 3
         L.wise_support_snapshot.argtypes = [S, ctypes.c_int32, V, ctypes.c_int32, V, ctypes.c_size_t, V]
         L.wise_support_restore.argtypes = [S, ctypes.c_int32, V, ctypes.c_int32, V, ctypes.c_size_t, V]
-        for f in ("wise_decode_dense", "wise_decode_discover", "wise_decode_sparse",
+        L.wise_decode_sparse_noalloc.argtypes = [P, S, V, V]
+        for f in ("wise_decode_sparse_noalloc", "wise_decode_dense", "wise_decode_discover", "wise_decode_sparse",
                   "wise_finish_select", "wise_discover_lse", "wise_compact_pages",
                   "wise_support_snapshot", "wise_support_restore"):
             getattr(L, f).restype = ctypes.c_int
@@ -147,6 +150,11 @@ def wise_compact_pages(a: WiseAttn, s: WiseSupport, row_mode: Optional[int], bt_
                        bt_out_stride: int, ctx_out: int, stream: int = 0) -> None:
     _check(lib().wise_compact_pages(ctypes.byref(a), ctypes.byref(s), row_mode, bt_out, bt_out_stride,
                                     ctx_out, stream), "wise_compact_pages")
+
+
+def wise_decode_sparse_noalloc(a: WiseAttn, s: WiseSupport, row_mode: Optional[int], stream: int = 0) -> None:
+    _check(lib().wise_decode_sparse_noalloc(ctypes.byref(a), ctypes.byref(s), row_mode, stream),
+           "wise_decode_sparse_noalloc")
 
 
 def wise_snapshot_bytes(layers: int, heads: int, words: int) -> int:

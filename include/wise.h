@@ -306,6 +306,26 @@ wise_status wise_support_snapshot(const wise_support *s, int32_t heads, const in
 wise_status wise_support_restore(const wise_support *s, int32_t heads, const int32_t *slots,
                                  int32_t count, const void *src, size_t src_bytes, void *stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): one whole
+ * (depth, layer) call -- exactly wise_decode_sparse(a, s, row_mode, ...)
+ * followed by wise_finish_select(a, s, ...), same kernels, same results --
+ * whose workspace is the library's own device buffer of
+ * WISE_SCRATCH_BYTES instead of a caller workspace.  Nothing is allocated:
+ * each GPU the library is loaded on holds one such buffer until the process
+ * ends.  Every call on a GPU uses that GPU's buffer, which keeps the last
+ * call's contents; calls that overlap on one GPU (other streams, other host
+ * threads) race on it and must be ordered by the caller.  Calls whose
+ * wise_workspace_size(rows, heads, head_dim, max_ctx) exceeds
+ * WISE_SCRATCH_BYTES return WISE_E_WORKSPACE before anything is enqueued
+ * (e.g. 64 rows x 16 heads x 8K tokens at head_dim 128 fit; 128 rows x 16
+ * heads x 32K do not).  Other errors as for the two calls it replaces.
+ */
+#define WISE_SCRATCH_BYTES ((size_t)32 << 20)
+wise_status wise_decode_sparse_noalloc(const wise_attn *a, const wise_support *s,
+                                       const uint8_t *row_mode, void *stream);
+
 /* Static, human-readable name of a status. */
 const char *wise_status_string(wise_status st);
 

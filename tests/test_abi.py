@@ -216,3 +216,20 @@ def test_missing_library_fails_loudly(monkeypatch):
         W.lib()
     with pytest.raises(RuntimeError, match="not built"):
         W.wise_workspace_size(1, 1, 128, 64)
+
+
+def test_noalloc_validation(lib):
+    """wise_decode_sparse_noalloc checks every host argument, and that the
+    call fits the library's static workspace, before it touches a device."""
+    a, s = good_attn(), good_support()
+
+    def na(a=a, s=s):
+        return lib.wise_decode_sparse_noalloc(None if a is None else ctypes.byref(a),
+                                              None if s is None else ctypes.byref(s), None, None)
+    assert na(a=None) == W.WISE_E_ARG
+    assert na(s=None) == W.WISE_E_ARG
+    assert na(a=good_attn(head_dim=96)) == W.WISE_E_UNSUPPORTED
+    assert na(s=good_support(eta=0.0)) == W.WISE_E_ARG
+    big = good_attn(rows=128, heads=16, max_ctx=32768, bt_stride=2048)
+    assert W.wise_workspace_size(128, 16, 128, 32768) > W.SCRATCH_BYTES
+    assert na(a=big, s=good_support(slots=128, words=32)) == W.WISE_E_WORKSPACE
