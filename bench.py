@@ -2,14 +2,20 @@
 
 A step is one token of every row through the workload's whole hot path:
 for the depth-schedule workloads, every depth (discover, discover-union,
-sparse, sparse) of every layer; for the mixed workload, the one launch that
+sparse, sparse) of every layer; for the mixed workloads, the one launch that
 mixes dense, discover and sparse rows (after untimed setup depths).  Each
-(depth, layer) call is the split-KV decode kernel (plus the plan kernel
-for calls with sparse rows whose units span several split workgroups) and
-the finish kernel.  Every input is resident in HBM before timing starts.
+(depth, layer) call is the library's decode call plus its finish call.
+Every input is resident in HBM before timing starts.
 
-Prints ONE JSON line.  ``value`` = decode-attention rows per second, where a
-row is one query row attended at one (depth, layer).
+Prints ONE JSON line.  ``value`` = decode-attention rows per second of the
+headline workload (ctx1k: 32 rows x 16 heads x 1K tokens), where a row is one
+query row attended at one (depth, layer), timed over whole steps replayed
+from HIP graphs.  ``contexts`` holds, for the 1K / 4K / 8K workloads and the
+ragged batch, every call kind's time -- the split kernel alone (stamped with
+its own start and stop) and the whole call (every kernel it launches, timed
+by HIP-graph replay of back-to-back calls) -- its algorithmic bytes, GB/s,
+fraction of the 8 TB/s HBM peak, sparse vs dense on the same KV, and the
+time a pure gather of the same K/V pages in items of the same length takes.
 """
 
 from __future__ import annotations
@@ -18,7 +24,9 @@ import argparse
 import ctypes
 import dataclasses
 import json
+import math
 import os
+import subprocess
 import sys
 import time
 
@@ -35,10 +43,26 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MODE_NAME = {W.WISE_DENSE: "dense", W.WISE_DISCOVER: "discover",
              W.WISE_DISCOVER_UNION: "discover_union", W.WISE_SPARSE: "sparse"}
 LSE_ROUTE = -1  # split_bytes key of discovery by the LSE route
+CALL_GRAPH_CALLS = 16   # back-to-back calls per captured graph (per-call time)
+CONTEXT_WORKLOADS = ("ctx1k", "match1k", "kbench1k", "ctx4k_24l", "match4k", "mix4k", "ctx8k_mixed",
+                     "match8k", "ragged")
+CONTEXT_OF = {"ctx1k": "1K", "match1k": "1K", "kbench1k": "1K", "ctx4k_24l": "4K", "match4k": "4K",
+              "mix4k": "4K", "ctx8k_mixed": "8K", "match8k": "8K", "ragged": "512-32K"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- bytes
+
+def attended_blocks(n, mode, support_words_rh):
+    """Blocks one (row, head) attends in a call of effective mode ``mode``."""
+    nb = (n + 31) // 32
+    if mode != W.WISE_SPARSE:
+        return np.arange(nb)
+    b = np.arange(nb)
+    return b[((support_words_rh[b >> 5] >> (b & 31).astype(np.uint32)) & 1).astype(bool)]
 
 
 def split_bytes(w, ctx, eff_modes, support_words):
@@ -95,22 +119,24 @@ def external_lse(layer_dev, ctx, page_size, scale=None):
     return out
 
 
-def cpu_baseline(w, min_s=10.0, max_rows=32):
-    """The fp64 oracle on a bounded sample of the same workload: up to
-    max_rows rows through the whole depth schedule, repeated until at least
-    min_s seconds of oracle time; single-threaded BLAS."""
+# ----------------------------------------------------------------------------- CPU baseline
+
+def _oracle_worker(w, rows, min_s):
+    """One worker's share of the CPU baseline: the fp64 oracle on ``rows``
+    through the whole depth schedule, repeated until at least ``min_s``
+    seconds of oracle time; one BLAS thread.  Inputs are generated first and
+    not timed."""
     from threadpoolctl import threadpool_limits
     from oracle import wise_oracle as O
     R = w.rows
-    sample_rows = list(range(min(R, max_rows)))
-    inputs = [synth.layer_inputs(w, depth, 0, rows=sample_rows) for depth in range(len(w.schedule))]
-    rows_done, t_total, tokens = 0, 0.0, 0
+    inputs = [synth.layer_inputs(w, depth, 0, rows=rows, workers=1) for depth in range(len(w.schedule))]
+    done, t_total, passes = 0, 0.0, 0
     with threadpool_limits(1):
-        while t_total < min_s:
+        while passes < 1 or t_total < min_s:   # pass 0 (first touch of the inputs) is not timed
+            passes += 1
             sup = np.zeros((R, 1, w.heads, (w.max_ctx + 1023) // 1024), np.uint32)
             tags = np.zeros((R, 1), O.TAG_DTYPE)
-            req = np.arange(R) + 1000
-            pos = np.zeros(R, np.int64)
+            req, pos = np.arange(R) + 1000, np.zeros(R, np.int64)
             for depth, mode in enumerate(w.schedule):
                 li = inputs[depth]
                 t0 = time.perf_counter()
@@ -118,15 +144,45 @@ def cpu_baseline(w, min_s=10.0, max_rows=32):
                                  ctx_len=li.ctx_len, page_size=w.page_size, num_pages=li.num_pages,
                                  max_ctx=w.max_ctx, modes=[mode] * R, support=sup, tags=tags,
                                  row_request=req, row_position=pos, required=max(1, w.discoveries),
-                                 eta=w.eta, rows=sample_rows)
-                t_total += time.perf_counter() - t0
+                                 eta=w.eta, rows=rows)
+                if passes > 1:
+                    t_total += time.perf_counter() - t0
+                    done += len(rows)
                 sup, tags = res.support, res.tags
-                rows_done += len(sample_rows)
-            tokens += 1
-    return {"value": round(rows_done / t_total, 2), "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(sample_rows)} of {R} rows x {len(w.schedule)} depths x {tokens} "
-                      f"repeats = {rows_done} row-calls in {t_total:.1f} s (fp64 numpy, 1 BLAS thread)"}
+    return done, t_total
 
+
+def host_facts():
+    model = "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return os.cpu_count() or 1, model
+
+
+def cpu_baseline(w, pool, workers, facts, min_s=1.5):
+    """The fp64 oracle on the headline workload's rows, split over ``workers``
+    processes (rows are independent through the whole schedule), each
+    repeating its rows' schedule for at least ``min_s`` s.  Throughput =
+    all row-calls / the slowest worker's oracle time."""
+    chunks = [list(map(int, c)) for c in np.array_split(np.arange(w.rows), min(workers, w.rows)) if len(c)]
+    res = [f.result() for f in [pool.submit(_oracle_worker, w, c, min_s) for c in chunks]]
+    done = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)
+    cpu = sum(r[1] for r in res)
+    nproc, model = facts
+    return {"value": round(done / wall, 2), "unit": "rows/s", "cores": len(chunks), "kind": "oracle",
+            "sample": f"all {w.rows} rows of {w.name} x {len(w.schedule)} depths, repeated; {done} row-calls "
+                      f"in {len(chunks)} processes ({cpu:.1f} s of oracle CPU time, slowest {wall:.2f} s); "
+                      f"fp64 numpy, 1 BLAS thread per process",
+            "nproc": nproc, "cpu_model": model, "blas_threads_per_process": 1}
+
+
+# ----------------------------------------------------------------------------- counters
 
 def split_source_digest() -> str:
     from block_sparse_paged_split_amd.profile_summary import split_source_digest as digest
@@ -151,50 +207,108 @@ def measured_traffic(workload):
     return rec.get("traffic_bytes_per_launch")
 
 
-class Plan:
-    """The calls of one step, per replica, and how to account for them."""
+# ----------------------------------------------------------------------------- read-ceiling probe
 
-    def __init__(self, w, args, dev):
+class ReadProbe:
+    """The benchmark's pure gather of K/V pages (libwise_probe.so)."""
+
+    def __init__(self):
+        from block_sparse_paged_split_amd import build
+        self.L = ctypes.CDLL(build.PROBE_LIB)
+        V, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        self.L.wise_read_probe.argtypes = [V, V, I64, I64, I64, I32, V, I64, V, I32, V, V, I32, V, V, V, V]
+        self.L.wise_read_probe.restype = ctypes.c_int
+
+    @staticmethod
+    def items_for(w, ctx, eff_modes, support_words, fused_units):
+        """(items [n, 4] int32, tiles int32, K/V bytes) of one call: every
+        (row, head)'s attended blocks cut into items as the library cuts
+        them -- a unit's tiles spread over four waves when the call finishes
+        inside the split kernel, else the call-wide rule (32 tiles when the
+        launch keeps >= 4096 such items, else 16 on that condition, else 8)."""
+        e = 2 if w.dtype == "bf16" else 4
+        lists = []
+        for r in range(w.rows):
+            for h in range(w.heads):
+                lists.append((r, h, attended_blocks(int(ctx[r]), int(eff_modes[r]),
+                                                    None if support_words is None else support_words[r, h])))
+        counts = np.array([len(b) for _, _, b in lists])
+        T = 8
+        for t in (32, 16):
+            if int(((counts + t - 1) // t).sum()) >= 4096:
+                T = t
+                break
+        items, tiles, nbytes = [], [], 0
+        for (r, h, blocks), c in zip(lists, counts):
+            n = int(ctx[r])
+            toks = np.minimum(32, n - 32 * blocks)
+            nbytes += int(2 * toks.sum() * w.head_dim * e)
+            t = max(1, -(-c // 4)) if fused_units else T
+            assert t <= 64 and (len(blocks) == 0 or (blocks.min() >= 0 and 32 * blocks.max() < n))
+            for i in range(0, c, t):
+                items.append((r, h, len(tiles) + i, min(t, c - i)))
+            tiles.extend(blocks.tolist())
+        return np.asarray(items, np.int32).reshape(-1, 4), np.asarray(tiles, np.int32), nbytes
+
+    def time(self, launches, stream, n_it, ev):
+        """Mean duration (ms) over n_it launches rotating over ``launches``."""
+        for it in range(n_it):
+            args = launches[it % len(launches)]
+            st = self.L.wise_read_probe(*args, ctypes.c_void_p(stream), ctypes.c_void_p(ev.handle(2 * it)),
+                                        ctypes.c_void_p(ev.handle(2 * it + 1)))
+            if st != 0:
+                raise RuntimeError(f"read probe failed ({st})")
+        import torch
+        torch.cuda.synchronize()
+        return float(np.mean([ev.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]))
+
+
+# ----------------------------------------------------------------------------- the calls of a step
+
+class Plan:
+    """The calls of one step, per replica (each replica with its own KV and
+    its own support state), and how to account for them."""
+
+    def __init__(self, w, replicas, kv_layers, dev):
         import torch
         self.w = w
         self.ctx = synth.context_lengths(w)
         self.mixed = w.mix is not None
-        # distinct KV sets: replicas x depths x (layer groups)
-        self.kv_layers = min(w.layers, args.kv_layers)
-        self.replicas = args.replicas
-        self.state = harness.SupportState(w.rows, w.heads, w.max_ctx, layers=w.layers, device=dev)
+        self.kv_layers = min(w.layers, kv_layers)
+        self.replicas = replicas
+        self.states = [harness.SupportState(w.rows, w.heads, w.max_ctx, layers=w.layers, device=dev)
+                       for _ in range(replicas)]
         self.ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx, device=dev)
         self.kv = {}
         t0 = time.time()
         depths = 3 if self.mixed else len(w.schedule)
-        for rep in range(self.replicas):
+        for rep in range(replicas):
             for depth in range(depths):
                 for lg in range(self.kv_layers):
                     wl = dataclasses.replace(w, seed=w.seed + 1000 * rep)
                     self.kv[(rep, depth, lg)] = harness.upload(synth.layer_inputs(wl, depth, lg), device=dev)
-                    log(f"inputs: replica {rep} depth {depth} layer-set {lg} ({time.time() - t0:.1f} s)")
+            log(f"  [{w.name}] inputs of replica {rep} ({time.time() - t0:.1f} s)")
         if self.mixed:
             modes, flagged = synth.mixed_row_modes(w)
-            self.row_modes = modes
-            self.flagged = flagged
+            self.row_modes, self.flagged = modes, flagged
             d0 = np.where(modes == W.WISE_DENSE, W.WISE_DENSE, W.WISE_DISCOVER).astype(np.uint8)
             d1 = np.where((modes == W.WISE_SPARSE) & ~flagged, W.WISE_DISCOVER_UNION,
                           W.WISE_DENSE).astype(np.uint8)
             self.setup_modes = [torch.from_numpy(d0).to(dev), torch.from_numpy(d1).to(dev)]
             self.mixed_modes = torch.from_numpy(modes.astype(np.uint8)).to(dev)
-        # calls[rep] = list of (PreparedCall, key) for one step
         self.calls = {}
-        for rep in range(self.replicas):
-            lst = []
+        req = max(1, w.discoveries)
+        for rep in range(replicas):
+            lst, st = [], self.states[rep]
             if self.mixed:
-                pc = harness.PreparedCall(self.kv[(rep, 2, 0)], self.ws, W.WISE_SPARSE, self.state,
-                                          required=max(1, w.discoveries), eta=w.eta, row_mode=self.mixed_modes)
+                pc = harness.PreparedCall(self.kv[(rep, 2, 0)], self.ws, W.WISE_SPARSE, st, required=req,
+                                          eta=w.eta, row_mode=self.mixed_modes)
                 lst.append((pc, ("mixed", 2, 0)))
             else:
                 for depth, mode in enumerate(w.schedule):
                     for layer in range(w.layers):
-                        pc = harness.PreparedCall(self.kv[(rep, depth, layer % self.kv_layers)], self.ws, mode,
-                                                  self.state, layer_idx=layer, required=max(1, w.discoveries), eta=w.eta)
+                        pc = harness.PreparedCall(self.kv[(rep, depth, layer % self.kv_layers)], self.ws, mode, st,
+                                                  layer_idx=layer, required=req, eta=w.eta)
                         lst.append((pc, (MODE_NAME[mode], depth, layer)))
             self.calls[rep] = lst
         self.calls_per_step = len(self.calls[0])
@@ -203,9 +317,9 @@ class Plan:
         """Untimed work that precedes a step: the discovery depths of the
         mixed launch's rows, or the fixed random support of a kernel-bench
         workload (with tags that admit reuse)."""
-        if self.w.fixed_density is not None:
+        w, st = self.w, self.states[rep]
+        if w.fixed_density is not None:
             import torch
-            w, st = self.w, self.state
             for layer in range(w.layers):
                 bits = synth.random_support(w, w.fixed_density, self.ctx, st.words, layer=layer)
                 st.support[:, layer] = torch.from_numpy(bits.view(np.int32)).to(st.support.device)
@@ -216,71 +330,57 @@ class Plan:
         if not self.mixed:
             return
         for depth in (0, 1):
-            harness.PreparedCall(self.kv[(rep, depth, 0)], self.ws, W.WISE_SPARSE, self.state,
-                                 required=max(1, self.w.discoveries), eta=self.w.eta,
+            harness.PreparedCall(self.kv[(rep, depth, 0)], self.ws, W.WISE_SPARSE, st,
+                                 required=max(1, w.discoveries), eta=w.eta,
                                  row_mode=self.setup_modes[depth]).run(stream)
 
     def eff_modes(self, key):
-        w = self.w
         if key[0] == "mixed":
             eff = self.row_modes.copy()
             eff[self.flagged] = W.WISE_DENSE
             return eff
         mode = {v: k for k, v in MODE_NAME.items()}[key[0]]
-        return np.full(w.rows, mode)
+        return np.full(self.w.rows, mode)
+
+    def counters(self):
+        return sum(st.counters.cpu().numpy() for st in self.states)
+
+    def free(self):
+        self.kv.clear()
+        self.calls.clear()
+        self.states.clear()
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ctx1k", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--replicas", type=int, default=None,
-                    help="distinct KV sets per depth, rotated across steps so the 256 MB MALL cannot "
-                         "serve repeats (default: 2 when one set is under 1 GB, else 1)")
-    ap.add_argument("--kv-layers", type=int, default=3,
-                    help="distinct KV sets per depth for multi-layer workloads, rotated over the layers")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense-reference", action="store_true")
-    ap.add_argument("--no-lse-route", action="store_true",
-                    help="skip the timing of discovery by the LSE route")
-    ap.add_argument("--no-page-route", action="store_true",
-                    help="skip the timing of the head-union page route")
-    ap.add_argument("--no-state-copy", action="store_true",
-                    help="skip the timing of the support/tag snapshot and restore")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time eager launches only (for counter-collection runs)")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="first run one plain device-to-device copy of this many MiB (a known-size "
-                         "reference for hardware byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
+def graph_of(fn, torch):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(int(torch.cuda.current_stream().cuda_stream))
+    return g
 
+
+def replay_ms(graphs, n, warmup, torch):
+    """Mean ms per replay over n replays rotating over ``graphs``."""
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(n):
+        graphs[i % len(graphs)].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
+def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=None, headline=False,
+            args=None):
+    """Everything measured on one workload; returns (entry, extras) where
+    extras holds what only the headline line reports."""
     import torch
-    W.lib()  # fails loudly if the HIP library is missing
-    w = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.replicas is None:
-        one_set = int(synth.context_lengths(w).sum()) * w.heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
-        args.replicas = 2 if one_set < (1 << 30) else 1
-    if args.calibrate_copy:
-        # a plain streaming kernel of known size (reads and writes MIB MiB)
-        src = torch.zeros(args.calibrate_copy << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        log(f"calibration kernel (neg): {args.calibrate_copy} MiB read + {args.calibrate_copy} MiB written")
-        del src, dst
-    plan = Plan(w, args, dev)
+    plan = Plan(w, replicas, kv_layers, dev)
     calls = plan.calls_per_step
-    ev = harness.HipEvents(2 * calls * args.steps)
-    main_stream = torch.cuda.current_stream()
-    sh = int(main_stream.cuda_stream)
+    ev = harness.HipEvents(2 * calls * steps)
+    sh = int(torch.cuda.current_stream().cuda_stream)
 
     def step(i, stream, timed=False):
         rep = i % plan.replicas
@@ -291,185 +391,232 @@ def main():
 
     for rep in range(plan.replicas):
         plan.setup(rep, sh)
-    for i in range(args.warmup):
+    for i in range(max(warmup, plan.replicas)):
         step(i, sh)
     torch.cuda.synchronize()
 
-    # ---- timed region 1 (eager): every split-KV launch bracketed by HIP events ----
-    plan.state.counters.zero_()
+    # ---- eager steps: every split-KV launch stamped with its own start and stop ----
+    for st in plan.states:
+        st.counters.zero_()
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, sh, timed=True)
     t_end.record()
     torch.cuda.synchronize()
-    eager_ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    ctr = plan.state.counters.cpu().numpy().copy()
-
-    # ---- timed region 2: the same steps replayed from HIP graphs ----
-    if args.no_graph:
-        ms_per_step = eager_ms_per_step
-    else:
-        graphs = []
-        for rep in range(plan.replicas):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(rep, int(torch.cuda.current_stream().cuda_stream))
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % plan.replicas].replay()
-        torch.cuda.synchronize()
-        t_start.record()
-        for i in range(args.steps):
-            graphs[i % plan.replicas].replay()
-        t_end.record()
-        torch.cuda.synchronize()
-        ms_per_step = t_start.elapsed_time(t_end) / args.steps
-
-    # ---- the same step with every call dense (no support state), replayed from
-    # HIP graphs: the step-level comparison the page makes between WISE decode and
-    # dense decode (its discovery depths cost a dense pass each; only the reuse
-    # depths can save) ----
-    dense_step_ms = None
-    if not args.no_graph and not args.no_dense_reference and not plan.mixed:
-        dgraphs = []
-        for rep in range(plan.replicas):
-            dcalls = [harness.PreparedCall(plan.kv[(rep, depth, layer % plan.kv_layers)], plan.ws, W.WISE_DENSE)
-                      for _, (_, depth, layer) in plan.calls[rep]]
-            for dc in dcalls:
-                dc.run(sh)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                cs = int(torch.cuda.current_stream().cuda_stream)
-                for dc in dcalls:
-                    dc.run(cs)
-            dgraphs.append(g)
-        for i in range(args.warmup):
-            dgraphs[i % plan.replicas].replay()
-        torch.cuda.synchronize()
-        t_start.record()
-        for i in range(args.steps):
-            dgraphs[i % plan.replicas].replay()
-        t_end.record()
-        torch.cuda.synchronize()
-        dense_step_ms = t_start.elapsed_time(t_end) / args.steps
-
-    # ---- per-mode split-kernel times and algorithmic bytes ----
-    # the support a sparse call reads is the one its replica's discovery
-    # depths wrote in the same step: rebuild it per replica (untimed)
-    sup_of = {}
+    eager_ms = t_start.elapsed_time(t_end) / steps
+    ctr = plan.counters()
     for rep in range(plan.replicas):
-        plan.setup(rep, sh)
-        step(rep, sh)
-        torch.cuda.synchronize()
-        sup_of[rep] = plan.state.support_numpy().copy()
-    per_mode = {}
-    bytes_cache = {}
-    for i in range(args.steps):
+        for pc, _ in plan.calls[rep]:
+            pc.set_events(None, None)
+
+    # ---- whole steps replayed from HIP graphs ----
+    step_ms = eager_ms
+    if graphs:
+        gs = [graph_of(lambda s, rep=rep: step(rep, s), torch) for rep in range(plan.replicas)]
+        step_ms = replay_ms(gs, steps, warmup, torch)
+        del gs
+
+    # ---- per-kind split times and algorithmic bytes (each replica's own support) ----
+    sup_of = {rep: plan.states[rep].support_numpy().copy() for rep in range(plan.replicas)}
+    kinds, bytes_cache = {}, {}
+    for i in range(steps):
         rep = i % plan.replicas
         for c, (pc, key) in enumerate(plan.calls[rep]):
-            name, depth, layer = key
+            name, _, layer = key
             ck = (rep, name, layer)
             if ck not in bytes_cache:
                 bytes_cache[ck] = split_bytes(w, plan.ctx, plan.eff_modes(key), sup_of[rep][:, layer])
-            m = per_mode.setdefault(name, {"ms": [], "bytes": []})
+            m = kinds.setdefault(name, {"ms": [], "bytes": []})
             m["ms"].append(ev.elapsed_ms(2 * (i * calls + c), 2 * (i * calls + c) + 1))
             m["bytes"].append(bytes_cache[ck])
-    modes_out = {}
+    out = {}
     tot_bytes = tot_ms = 0.0
-    for key, m in per_mode.items():
-        ms = np.asarray(m["ms"])
-        by = np.asarray(m["bytes"], dtype=np.float64)
-        modes_out[key] = {"split_us": round(float(ms.mean()) * 1e3, 2),
-                          "split_us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
-                          "split_us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2),
-                          "algorithmic_MB": round(float(by.mean()) / 1e6, 3),
-                          "GBps": round(float(by.sum()) / (float(ms.sum()) * 1e-3) / 1e9, 1)}
+    for name, m in kinds.items():
+        ms, by = np.asarray(m["ms"]), np.asarray(m["bytes"], np.float64)
+        out[name] = {"split_us": round(float(ms.mean()) * 1e3, 2),
+                     "split_us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                     "split_us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2),
+                     "algorithmic_MB": round(float(by.mean()) / 1e6, 3),
+                     "split_GBps": round(float(by.sum()) / (float(ms.sum()) * 1e-3) / 1e9, 1)}
         tot_bytes += float(by.sum())
         tot_ms += float(ms.sum())
     achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
 
-    # ---- dense reference: the dense decode of the same rows, back to back, rotating
-    # over every KV set of the run (so that no call rereads what the last one left
-    # in the 256 MB MALL; the sets hold the same shapes as the sparse calls' KV) ----
-    if not args.no_dense_reference and any(key[0] in ("sparse", "mixed") for _, key in plan.calls[0]):
-        dpcs = [harness.PreparedCall(plan.kv[k], plan.ws, W.WISE_DENSE) for k in sorted(plan.kv)]
-        n_it = max(16, 2 * len(dpcs))
-        ev2 = harness.HipEvents(2 * n_it)
-        for dpc in dpcs[:2]:
-            dpc.set_events(None, None)
-            dpc.run(sh)
-        for it in range(n_it):
-            dpc = dpcs[it % len(dpcs)]
-            dpc.set_events(ev2.handle(2 * it), ev2.handle(2 * it + 1))
-            dpc.run(sh)
-        torch.cuda.synchronize()
-        dense_ms = [ev2.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]
-        for dpc in dpcs:
-            dpc.set_events(None, None)
-        if dense_ms:
-            dms = float(np.mean(dense_ms))
-            dbytes = split_bytes(w, plan.ctx, np.full(w.rows, W.WISE_DENSE), None)
-            key = "mixed" if plan.mixed else "sparse"
-            modes_out["dense_same_kv"] = {"split_us": round(dms * 1e3, 2), "algorithmic_MB": round(dbytes / 1e6, 3),
-                                          "GBps": round(dbytes / (dms * 1e-3) / 1e9, 1)}
-            modes_out[key]["speedup_vs_dense"] = round(dms * 1e3 / modes_out[key]["split_us"], 3)
+    # ---- whole calls: every kernel a call launches, by graph replay of back-to-back
+    # calls (replicas rotate, each with its own state, so a reuse call reads the
+    # support its own discovery depths wrote); kinds in schedule order ----
+    dense_pcs = [harness.PreparedCall(plan.kv[k], plan.ws, W.WISE_DENSE) for k in sorted(plan.kv)]
+    groups = []
+    for name in kinds:
+        pcs = [pc for rep in range(plan.replicas) for pc, key in plan.calls[rep] if key[0] == name]
+        groups.append((name, pcs))
+    groups.append(("dense_same_kv", dense_pcs))
+    dense_bytes = split_bytes(w, plan.ctx, np.full(w.rows, W.WISE_DENSE), None)
+    if graphs:
+        for name, pcs in groups:
+            k = max(CALL_GRAPH_CALLS, len(pcs))
 
-    # ---- discovery by the LSE route (K reread, no output), rotating over every KV set ----
+            def run_k(s, pcs=pcs, k=k):
+                for j in range(k):
+                    pcs[j % len(pcs)].run(s)
+            run_k(sh)
+            torch.cuda.synchronize()
+            g = graph_of(run_k, torch)
+            call_us = replay_ms([g], 3, 1, torch) / k * 1e3
+            del g
+            if name == "dense_same_kv":
+                out[name] = {"algorithmic_MB": round(dense_bytes / 1e6, 3)}
+            mb = out[name]["algorithmic_MB"]
+            out[name].update({"call_us": round(call_us, 2), "call_GBps": round(mb * 1e6 / (call_us * 1e-6) / 1e9, 1),
+                              "call_frac": round(mb * 1e6 / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    # split-stamped dense reference, rotating over every KV set of the run
+    n_it = max(16, 2 * len(dense_pcs))
+    ev2 = harness.HipEvents(2 * n_it)
+    for it in range(n_it):
+        pc = dense_pcs[it % len(dense_pcs)]
+        pc.set_events(ev2.handle(2 * it), ev2.handle(2 * it + 1))
+        pc.run(sh)
+    torch.cuda.synchronize()
+    dms = float(np.mean([ev2.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]))
+    for pc in dense_pcs:
+        pc.set_events(None, None)
+    out.setdefault("dense_same_kv", {"algorithmic_MB": round(dense_bytes / 1e6, 3)})
+    out["dense_same_kv"].update({"split_us": round(dms * 1e3, 2),
+                                 "split_GBps": round(dense_bytes / (dms * 1e-3) / 1e9, 1)})
+    reuse = "mixed" if plan.mixed else ("sparse" if "sparse" in out else None)
+    if reuse:
+        out[reuse]["speedup_vs_dense_split"] = round(out["dense_same_kv"]["split_us"] / out[reuse]["split_us"], 3)
+        if "call_us" in out[reuse]:
+            out[reuse]["speedup_vs_dense_call"] = round(out["dense_same_kv"]["call_us"] / out[reuse]["call_us"], 3)
+
+    # ---- read ceiling: a pure gather of the same K/V pages in items of the same length ----
+    if probe is not None and reuse:
+        e = 2 if w.dtype == "bf16" else 4
+        fused = (w.max_ctx + 31) // 32 <= 32
+        ceil = {}
+        for name, key_kind in ((reuse, reuse), ("dense_same_kv", None)):
+            launches, nbytes, keep = [], [], []
+            for rep in range(plan.replicas):
+                if key_kind is None:
+                    lays = [(plan.kv[(rep, d, 0)], np.full(w.rows, W.WISE_DENSE), None)
+                            for d in range(3 if plan.mixed else len(w.schedule))]
+                else:
+                    lays = [(pc_key_kv, plan.eff_modes(key), sup_of[rep][:, key[2]])
+                            for pc, key in plan.calls[rep] if key[0] == key_kind
+                            for pc_key_kv in [plan.kv[(rep, key[1], key[2] % plan.kv_layers)]]]
+                for kv, eff, sw in lays:
+                    items, tiles, nb = ReadProbe.items_for(w, plan.ctx, eff, sw, fused)
+                    it_d = torch.from_numpy(items).to(dev)
+                    ti_d = torch.from_numpy(tiles).to(dev)
+                    sink = torch.empty(len(items), dtype=torch.int32, device=dev)
+                    keep += [it_d, ti_d, sink]
+                    sp, sh_, st_, _ = kv.k.stride()
+                    launches.append((kv.k.data_ptr(), kv.v.data_ptr(), sp * e, sh_ * e, st_ * e, w.head_dim * e,
+                                     kv.block_table.data_ptr(), kv.block_table.stride(0), kv.ctx_len.data_ptr(),
+                                     int(math.log2(w.page_size)), it_d.data_ptr(), ti_d.data_ptr(), len(items),
+                                     sink.data_ptr()))
+                    nbytes.append(nb)
+            n_it = max(16, 2 * len(launches))
+            ev3 = harness.HipEvents(2 * n_it)
+            probe.time(launches, sh, min(4, len(launches)), ev3)     # warm-up
+            ms = probe.time(launches, sh, n_it, ev3)
+            mb = float(np.mean([nbytes[i % len(nbytes)] for i in range(n_it)]))
+            ceil[name] = {"us": round(ms * 1e3, 2), "kv_MB": round(mb / 1e6, 3),
+                          "GBps": round(mb / (ms * 1e-3) / 1e9, 1)}
+        out["read_ceiling"] = ceil
+
+    if w.fixed_density is not None:
+        # no discovery depth: the density of the support set directly
+        nb = (plan.ctx.astype(np.int64) + 31) // 32
+        sup = sup_of[0][:, 0]
+        set_bits = sum(len(attended_blocks(int(plan.ctx[r]), W.WISE_SPARSE, sup[r, h]))
+                       for r in range(w.rows) for h in range(w.heads))
+        density = set_bits / float(nb.sum() * w.heads)
+    else:
+        density = float(ctr[W.CTR_SELECTED] / max(1, ctr[W.CTR_CAUSAL]))
+    entry = {"context": CONTEXT_OF.get(w.name, ""), "rows": w.rows,
+             "ctx": w.ctx if w.ctx else f"{int(plan.ctx.min())}..{int(plan.ctx.max())}",
+             "layers": w.layers, "union_density": round(density, 4),
+             "fallbacks_per_step": round(float(ctr[W.CTR_FALLBACKS]) / steps, 2),
+             "errors": int(ctr[W.CTR_ERRORS]),
+             "ms_per_step": round(step_ms, 4), "rows_per_s": round(w.rows * calls / (step_ms * 1e-3), 1),
+             "calls": out}
+    extras = {"plan": plan, "eager_ms": eager_ms, "step_ms": step_ms, "achieved": achieved, "ctr": ctr,
+              "calls": calls, "sh": sh}
+    if headline:
+        extras.update(headline_legs(w, plan, dev, sh, steps, warmup, args, out, graphs))
+    return entry, extras
+
+
+def headline_legs(w, plan, dev, sh, steps, warmup, args, out, graphs):
+    """The legs only the headline line reports: the all-dense step, the LSE
+    route, the head-union page route and the support snapshot/restore."""
+    import torch
+    res = {}
+    calls_per_rep = plan.calls
+    if graphs and not plan.mixed:
+        dgraphs = []
+        for rep in range(plan.replicas):
+            dcalls = [harness.PreparedCall(plan.kv[(rep, depth, layer % plan.kv_layers)], plan.ws, W.WISE_DENSE)
+                      for _, (_, depth, layer) in calls_per_rep[rep]]
+
+            def run(s, dcalls=dcalls):
+                for dc in dcalls:
+                    dc.run(s)
+            run(sh)
+            dgraphs.append(graph_of(run, torch))
+        dense_step_ms = replay_ms(dgraphs, steps, warmup, torch)
+        del dgraphs
+        res["dense_step"] = {"ms_per_step": round(dense_step_ms, 4),
+                             "note": "every call of the step dense, HIP graph replay"}
+    st0 = plan.states[0]
     if not args.no_lse_route and not plan.mixed:
-        sets = []
-        for key, layer_dev in plan.kv.items():
-            a = layer_dev.attn()
-            lse = external_lse(layer_dev, plan.ctx, w.page_size)
-            sets.append((a, lse))
-        s = plan.state.view(0, 1, w.eta)
+        sets = [(layer_dev.attn(), external_lse(layer_dev, plan.ctx, w.page_size)) for layer_dev in plan.kv.values()]
+        s = st0.view(0, 1, w.eta)
         n_it = 4 * len(sets)
         ev3 = harness.HipEvents(2 * n_it + 2)
         for a, lse in sets[:2]:
             W.wise_discover_lse(a, s, False, int(lse.data_ptr()), plan.ws.ptr, plan.ws.nbytes, sh)
         ev3.record(2 * n_it, sh)
-        for it in range(n_it):       # back to back, like the timed steps
+        for it in range(n_it):
             a, lse = sets[it % len(sets)]
             a.ev_split_begin, a.ev_split_end = ev3.handle(2 * it), ev3.handle(2 * it + 1)
             W.wise_discover_lse(a, s, False, int(lse.data_ptr()), plan.ws.ptr, plan.ws.nbytes, sh)
         ev3.record(2 * n_it + 1, sh)
         torch.cuda.synchronize()
-        split_ms = [ev3.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]
-        call_ms = [ev3.elapsed_ms(2 * n_it, 2 * n_it + 1) / n_it]
+        sms = float(np.mean([ev3.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]))
+        lbytes = split_bytes(w, plan.ctx, np.full(w.rows, LSE_ROUTE), None)
+        res["lse_discover"] = {"split_us": round(sms * 1e3, 2),
+                               "call_us_eager": round(ev3.elapsed_ms(2 * n_it, 2 * n_it + 1) / n_it * 1e3, 2),
+                               "algorithmic_MB": round(lbytes / 1e6, 3),
+                               "split_GBps": round(lbytes / (sms * 1e-3) / 1e9, 1),
+                               "note": "K-only split + LSE selection, eager back-to-back calls"}
         for a, _ in sets:
             a.ev_split_begin = a.ev_split_end = None
-        lbytes = split_bytes(w, plan.ctx, np.full(w.rows, LSE_ROUTE), None)
-        sms = float(np.mean(split_ms))
-        modes_out["lse_discover"] = {"split_us": round(sms * 1e3, 2),
-                                     "call_us": round(float(np.mean(call_ms)) * 1e3, 2),
-                                     "algorithmic_MB": round(lbytes / 1e6, 3),
-                                     "GBps": round(lbytes / (sms * 1e-3) / 1e9, 1),
-                                     "note": "K-only split + LSE selection, eager back-to-back calls; "
-                                             "not part of a step"}
-
-    # ---- reuse depths by the head-union page route: compaction + dense decode over it ----
+        # restore replica 0's own schedule state
+        plan.setup(0, sh)
+        for pc, _ in plan.calls[0]:
+            pc.run(sh)
+        torch.cuda.synchronize()
     if not args.no_page_route and not plan.mixed:
         sparse_keys = [key for _, key in plan.calls[0] if key[0] == "sparse"]
         if sparse_keys:
-            plan.setup(0, sh)
-            step(0, sh)                      # replica 0's discovery supports, untimed
-            torch.cuda.synchronize()
             pus = [(harness.PageUnion(plan.kv[(0, depth, layer % plan.kv_layers)]), layer)
                    for _, depth, layer in sparse_keys]
             for pu, layer in pus:
-                pu.compact(plan.state, layer, max(1, w.discoveries), stream=sh)
+                pu.compact(st0, layer, max(1, w.discoveries), stream=sh)
                 pu.attend(plan.ws, stream=sh)
             n_it = max(20, 2 * len(pus))
             ev4 = harness.HipEvents(4 * n_it + 2)
             L = W.lib()
-            prepared = []                    # ctypes arguments built once: issuing stays ahead of the GPU
+            prepared = []
             for pu, layer in pus:
-                a_c, s_c, a_d = pu.layer.attn(), plan.state.view(layer, max(1, w.discoveries), w.eta), pu.attend_attn()
+                a_c, s_c, a_d = pu.layer.attn(), st0.view(layer, max(1, w.discoveries), w.eta), pu.attend_attn()
                 prepared.append((a_c, s_c, a_d, int(pu.bt.data_ptr()), pu.bt.stride(0), int(pu.ctx.data_ptr())))
             ev4.record(4 * n_it, sh)
-            for it in range(n_it):           # back to back
+            for it in range(n_it):
                 a_c, s_c, a_d, bt_p, bt_s, ctx_p = prepared[it % len(prepared)]
                 ev4.record(4 * it, sh)
                 st = L.wise_compact_pages(ctypes.byref(a_c), ctypes.byref(s_c), None, bt_p, bt_s, ctx_p, sh)
@@ -492,80 +639,168 @@ def main():
                 kept_pages += int(((c + P - 1) // P).sum())
                 all_pages += int(((plan.ctx.astype(np.int64) + P - 1) // P).sum())
             sbytes = float(np.mean([by[it % len(pus)] for it in range(n_it)]))
-            total_us = float(comp_ms.mean() + split_ms.mean()) * 1e3
-            entry = {"compact_us": round(float(comp_ms.mean()) * 1e3, 2),
-                     "split_us": round(float(split_ms.mean()) * 1e3, 2),
-                     "call_us": round(ev4.elapsed_ms(4 * n_it, 4 * n_it + 1) / n_it * 1e3, 2),
-                     "page_density": round(kept_pages / max(1, all_pages), 4),
-                     "algorithmic_MB": round(sbytes / 1e6, 3),
-                     "GBps": round(sbytes / (float(split_ms.mean()) * 1e-3) / 1e9, 1),
-                     "note": "head-union pages of the reuse depths; compaction + dense decode over "
-                             "the compacted table, eager back-to-back"}
-            if "dense_same_kv" in modes_out:
-                entry["speedup_vs_dense"] = round(modes_out["dense_same_kv"]["split_us"] / total_us, 3)
-            modes_out["page_union"] = entry
-
-    if dense_step_ms is not None:
-        modes_out["dense_step"] = {"ms_per_step": round(dense_step_ms, 4),
-                                   "wise_step_speedup": round(dense_step_ms / ms_per_step, 3),
-                                   "note": "every call of the step dense, HIP graph replay; "
-                                           "wise_step_speedup = dense step time / WISE step time"}
-
-    # ---- support/tag snapshot and restore of every row's slot (KV offload and resume) ----
+            res["page_union"] = {"compact_us": round(float(comp_ms.mean()) * 1e3, 2),
+                                 "split_us": round(float(split_ms.mean()) * 1e3, 2),
+                                 "call_us_eager": round(ev4.elapsed_ms(4 * n_it, 4 * n_it + 1) / n_it * 1e3, 2),
+                                 "page_density": round(kept_pages / max(1, all_pages), 4),
+                                 "algorithmic_MB": round(sbytes / 1e6, 3),
+                                 "split_GBps": round(sbytes / (float(split_ms.mean()) * 1e-3) / 1e9, 1),
+                                 "note": "head-union pages of the reuse depths; compaction + dense decode over "
+                                         "the compacted table, eager back-to-back"}
     if not args.no_state_copy:
-        st_ = plan.state
         slots = torch.arange(w.rows, dtype=torch.int32, device=dev)
-        rec = st_.record_bytes()
+        rec = st0.record_bytes()
         records = torch.empty(w.rows * rec, dtype=torch.uint8, device=dev)
         n_it = 20
         ev5 = harness.HipEvents(4 * n_it)
-        st_.snapshot(slots, records, sh)
-        st_.restore(slots, records, sh)
+        st0.snapshot(slots, records, sh)
+        st0.restore(slots, records, sh)
         for it in range(n_it):
             ev5.record(4 * it, sh)
-            st_.snapshot(slots, records, sh)
+            st0.snapshot(slots, records, sh)
             ev5.record(4 * it + 1, sh)
             ev5.record(4 * it + 2, sh)
-            st_.restore(slots, records, sh)
+            st0.restore(slots, records, sh)
             ev5.record(4 * it + 3, sh)
         torch.cuda.synchronize()
-        snap_ms = np.mean([ev5.elapsed_ms(4 * it, 4 * it + 1) for it in range(n_it)])
-        rest_ms = np.mean([ev5.elapsed_ms(4 * it + 2, 4 * it + 3) for it in range(n_it)])
-        modes_out["offload_state"] = {"snapshot_us": round(float(snap_ms) * 1e3, 2),
-                                      "restore_us": round(float(rest_ms) * 1e3, 2),
-                                      "bytes_per_slot": rec, "slots": w.rows,
-                                      "note": "support words of every layer and head + tags, all rows' "
-                                              "slots; each copy reads and writes slots x bytes_per_slot"}
+        res["offload_state"] = {
+            "snapshot_us": round(float(np.mean([ev5.elapsed_ms(4 * i, 4 * i + 1) for i in range(n_it)])) * 1e3, 2),
+            "restore_us": round(float(np.mean([ev5.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(n_it)])) * 1e3, 2),
+            "bytes_per_slot": rec, "slots": w.rows}
+    return res
 
-    rows_per_step = w.rows * calls
+
+def default_replicas(w):
+    """Distinct KV sets per depth, rotated so the 256 MB MALL cannot serve
+    repeats: 1K workloads read a few tens to a few hundred MB per call, so
+    they rotate six; larger ones rotate one or two."""
+    one_set = int(synth.context_lengths(w).sum()) * w.heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
+    if w.max_ctx <= 1024:
+        return 6
+    return 2 if one_set < (1 << 30) else 1
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ctx1k", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=None, help="distinct KV sets per depth (default: by size)")
+    ap.add_argument("--kv-layers", type=int, default=3,
+                    help="distinct KV sets per depth for multi-layer workloads, rotated over the layers")
+    ap.add_argument("--contexts", default=",".join(CONTEXT_WORKLOADS),
+                    help="workloads measured per call in the contexts block ('' for none)")
+    ap.add_argument("--context-steps", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true")
+    ap.add_argument("--no-lse-route", action="store_true")
+    ap.add_argument("--no-page-route", action="store_true")
+    ap.add_argument("--no-state-copy", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (for counter-collection runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run one plain device-to-device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    # the CPU baseline's worker processes fork from a server started before
+    # this process touches the GPU
+    pool, workers = None, 0
+    facts = host_facts()
+    if not args.no_cpu_baseline:
+        import concurrent.futures
+        import multiprocessing
+        import multiprocessing.forkserver as fs
+        ctx = multiprocessing.get_context("forkserver")
+        ctx.set_forkserver_preload(["numpy", "oracle.wise_oracle", "block_sparse_paged_split_amd.synth"])
+        fs.ensure_running()
+        workers = max(1, min(16, os.cpu_count() or 1))   # the host share of one GPU
+        pool = concurrent.futures.ProcessPoolExecutor(workers, mp_context=ctx)
+
+    import torch
+    W.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    graphs = not args.no_graph
+    probe = None if args.no_read_ceiling else ReadProbe()
+    if args.calibrate_copy:
+        src = torch.zeros(args.calibrate_copy << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration kernel (neg): {args.calibrate_copy} MiB read + {args.calibrate_copy} MiB written")
+        del src, dst
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"headline workload {w.name}")
+    head, ex = measure(w, dev, steps=args.steps, warmup=args.warmup,
+                       replicas=args.replicas or default_replicas(w), kv_layers=args.kv_layers, graphs=graphs,
+                       probe=probe, headline=True, args=args)
+    plan = ex["plan"]
+    rows_per_step = w.rows * ex["calls"]
+    achieved = ex["achieved"]   # every timed split launch's algorithmic bytes / its stamped duration
+    modes_out = dict(head["calls"])
+    for k in ("dense_step", "lse_discover", "page_union", "offload_state"):
+        if k in ex:
+            modes_out[k] = ex[k]
+    if "dense_step" in modes_out:
+        modes_out["dense_step"]["wise_step_speedup"] = round(modes_out["dense_step"]["ms_per_step"] / ex["step_ms"], 3)
+    ctr = ex["ctr"]
+    config = {"workload": w.name, "rows": w.rows, "heads": w.heads, "head_dim": w.head_dim,
+              "ctx": head["ctx"], "page_size": w.page_size, "layers": w.layers,
+              "schedule": "mixed launch" if plan.mixed else list(w.schedule), "eta": w.eta,
+              "row_calls_per_step": rows_per_step, "kv_replicas": plan.replicas,
+              "kv_sets_per_depth": plan.kv_layers,
+              "timing": "eager launches" if args.no_graph else "HIP graph replay of whole steps",
+              "union_density": head["union_density"], "fallbacks_per_step": head["fallbacks_per_step"],
+              "errors": head["errors"]}
+    plan.free()
+    del ex, plan
+    torch.cuda.empty_cache()
+
+    contexts = {}
+    for name in [x for x in args.contexts.split(",") if x]:
+        if name == w.name:
+            contexts[name] = head
+            continue
+        wc = synth.WORKLOADS[name]
+        if wc.layers > 1:   # per-call figures need one layer of the same shape
+            wc = dataclasses.replace(wc, layers=1)
+        log(f"context workload {name}")
+        entry, ex_c = measure(wc, dev, steps=args.context_steps, warmup=2, replicas=default_replicas(wc),
+                              kv_layers=1, graphs=graphs, probe=probe)
+        ex_c["plan"].free()
+        del ex_c
+        torch.cuda.empty_cache()
+        contexts[name] = entry
+
     out = {
         "metric": "decode-attn rows/s + achieved HBM GB/s (sparse vs dense), ctx 1K/4K/8K",
-        "value": round(rows_per_step / (ms_per_step * 1e-3), 1),
+        "value": round(rows_per_step / (head["ms_per_step"] * 1e-3), 1),
         "unit": "rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "eager_ms_per_step": round(eager_ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "rows": w.rows, "heads": w.heads, "head_dim": w.head_dim,
-                   "ctx": w.ctx if w.ctx else f"{int(plan.ctx.min())}..{int(plan.ctx.max())}",
-                   "page_size": w.page_size, "layers": w.layers,
-                   "schedule": "mixed launch" if plan.mixed else list(w.schedule), "eta": w.eta,
-                   "row_calls_per_step": rows_per_step, "kv_replicas": plan.replicas,
-                   "kv_sets_per_depth": plan.kv_layers,
-                   "timing": "eager launches" if args.no_graph else "HIP graph replay of whole steps",
-                   "union_density": round(float(ctr[W.CTR_SELECTED] / max(1, ctr[W.CTR_CAUSAL])), 4),
-                   "fallbacks_per_step": round(float(ctr[W.CTR_FALLBACKS]) / args.steps, 2),
-                   "errors": int(ctr[W.CTR_ERRORS])},
+        "config": config,
         "modes": modes_out,
-        "roofline": {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name)},
+        "contexts": contexts,
+        "roofline": None,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        log("cpu baseline: timing the oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(w)
+    # roofline of the dominant kernel: the split kernel of the headline's calls
+    out["roofline"] = {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 1),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                       "traffic": measured_traffic(w.name)}
+    if pool is not None:
+        log("cpu baseline: the oracle on the headline rows, in worker processes")
+        out["cpu_baseline"] = cpu_baseline(w, pool, workers, facts)
+        pool.shutdown()
     print(json.dumps(out), flush=True)
 
 

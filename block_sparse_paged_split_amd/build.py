@@ -22,8 +22,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: ROCm is required to build libwise")
 
 
-def command(out: str = LIB, extra=()):
-    src = [os.path.join(PKG, "csrc", s) for s in SOURCES]
+def command(out: str = LIB, extra=(), sources=SOURCES):
+    src = [os.path.join(PKG, "csrc", s) for s in sources]
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 instructions are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,16 +31,26 @@ def command(out: str = LIB, extra=()):
             *extra, *src, "-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+# The benchmark's read-ceiling probe (not part of libwise; only bench.py loads it).
+PROBE_SOURCES = ["read_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libwise_probe.so")
+
+
+def _compile(cmd, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [tmp if c == out else c for c in cmd]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("libwise build failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"build of {os.path.basename(out)} failed")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(command(LIB), LIB, verbose)
+    _compile(command(PROBE_LIB, sources=PROBE_SOURCES), PROBE_LIB, verbose)
     return LIB
 
 

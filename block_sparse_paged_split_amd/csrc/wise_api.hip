@@ -222,7 +222,8 @@ wise_status decode(const wise_attn *a, const wise_support *s, int uniform_mode, 
   // per unit and no empty slots worth removing.
   // units that fit one split workgroup are also finished by it (the paired
   // wise_finish_select then has nothing left to do)
-  const bool fused = fused_finish_shape(L, a->heads, a->dtype);
+  p.fused_waves = fused_waves(L, a->heads, a->dtype, stateful);
+  const bool fused = p.fused_waves > 0;
   p.lse = lse;
   const bool listed = !fused && (row_mode != nullptr || uniform_mode == WISE_SPARSE) && p.chunk_groups > 1;
   // a static call with no sparse rows: longer items for large launches (the
@@ -256,7 +257,7 @@ wise_status finish(const wise_attn *a, const wise_support *s, const float *lse, 
   st = check_ws(ws, ws_bytes, L);
   if (st != WISE_OK) return st;
   // the decode call already finished these units (see decode())
-  if (fused_finish_shape(L, a->heads, a->dtype)) return WISE_OK;
+  if (fused_waves(L, a->heads, a->dtype, s != nullptr) > 0) return WISE_OK;
   char *w = static_cast<char *>(ws);
   FinishParams p{};
   p.rows = a->rows;

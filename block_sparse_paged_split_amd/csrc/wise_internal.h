@@ -32,7 +32,8 @@ __host__ __device__ inline int encode_row(int eff, int req) { return (eff & 0xF)
 int tiles_per_item(int max_blocks, int64_t units);
 constexpr int64_t kSmallLaunchItems = 1024;  // below this many 8-tile items a launch cuts items shorter
 constexpr int kMaxFusedItems = 16;            // items (waves) of one fused split + finish workgroup
-constexpr int kMaxFusedBlocks = 64;           // blocks of a fused unit (one per lane in its selection)
+constexpr int kMaxFusedBlocks = 64;           // blocks of a short fused unit (one per lane in its selection)
+constexpr int kWideFusedBlocks = 256;         // blocks of a long fused unit (four per lane in its selection)
 
 // Large launches run longer items: every item leaves a partial (m, l, acc)
 // in HBM, and those writes, interleaved with the K/V stream, cost far more
@@ -65,6 +66,7 @@ struct SplitParams {
   int32_t rows, heads, max_ctx, max_blocks, num_pages, page_shift;
   float qk_scale_log2;  // softmax scale * log2(e)
   int32_t tiles_per_item, items_per_unit, chunk_groups;
+  int32_t fused_waves;  // fused split + finish: waves per workgroup (one workgroup per unit)
   int32_t long_items;  // listed calls: the plan kernel may lengthen items to 16 or 32 tiles
   // requested modes
   const uint8_t *row_mode;  // NULL: every row uniform_mode
@@ -161,19 +163,38 @@ void state_record_layout(int layers, int heads, int words, size_t *tags_offset, 
 hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, bool fused,
                         int cus, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 
-// The finish is fused into the split kernel when every unit's items fit one
-// split workgroup (one wave per item): up to 4 items at eight tiles each, or
-// up to 16 (8 for fp32 at head_dim 128, whose waves need more than 128
-// registers) when a small launch cut its items shorter; a unit has at most 64
-// blocks, and a row's heads fit the 8-bit arrival count kept in the tag's
-// reserved word.  Decode and finish calls take the same decision from the
-// same sizes.
+// The finish is fused into the split kernel, one workgroup per unit whose
+// waves split the unit's tiles evenly and leave their partials in LDS, when
+// a row's heads fit the 8-bit arrival count kept in the tag's reserved word
+// and either
+//  * a unit has at most 64 blocks and its items at the layout's length fit
+//    the workgroup: up to 4 items at eight tiles each, or up to 16 (8 for
+//    fp32 at head_dim 128, whose waves need more than 128 registers) when a
+//    small launch cut its items shorter -- the workgroup has as many waves
+//    as the unit has items; or
+//  * a unit has at most 256 blocks (contexts up to 8K): 8 waves share its
+//    tiles when the launch has at least 512 units, 16 in smaller launches
+//    (fp32 at head_dim 128: 8) -- except a small call with no support state
+//    (plain dense decode), which keeps the static grid: its four-wave
+//    workgroups of eight-tile items fill every wave slot of the chip in one
+//    round, where 16-wave workgroups (one per CU at this kernel's register
+//    count) would take two.
+// Returns the waves per workgroup, 0 when the call is not fused.  Decode and
+// finish calls take the same decision from the same sizes and from whether
+// they were given a support state.
+constexpr int64_t kWideFusedMinUnits = 512;
 inline int fused_max_items(const Layout &L, int dtype) {
   if (L.tiles_per_item >= 8) return kWavesPerGroup;
   return (dtype == WISE_F32 && L.head_dim == 128) ? 8 : kMaxFusedItems;
 }
-inline bool fused_finish_shape(const Layout &L, int heads, int dtype) {
-  return L.items_per_unit <= fused_max_items(L, dtype) && L.max_blocks <= kMaxFusedBlocks && heads <= 255;
+inline int fused_waves(const Layout &L, int heads, int dtype, bool stateful) {
+  if (heads > 255) return 0;
+  if (L.max_blocks <= kMaxFusedBlocks && L.items_per_unit <= fused_max_items(L, dtype))
+    return L.items_per_unit <= 4 ? 4 : L.items_per_unit <= 8 ? 8 : 16;
+  if (L.max_blocks > kWideFusedBlocks) return 0;
+  const bool large = static_cast<int64_t>(L.rows) * heads >= kWideFusedMinUnits;
+  if (!large && !stateful) return 0;
+  return (large || (dtype == WISE_F32 && L.head_dim == 128)) ? 8 : 16;
 }
 hipError_t launch_finish(const FinishParams &p, hipStream_t stream);
 hipError_t launch_compact_pages(const PageParams &p, hipStream_t stream);

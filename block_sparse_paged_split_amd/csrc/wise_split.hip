@@ -520,10 +520,10 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
 // unit of the row planned from the tag before any head arrives, so the
 // update cannot race with a plan.
 // ---------------------------------------------------------------------------
-template <int D, bool kKOnly>
+template <int D, bool kKOnly, int MAXB>
 __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan &rp, int u, int h, int nb,
                                              int items, const float *s_acc, const float2 *s_ml,
-                                             const float2 *s_st, float *s_w, int lane) {
+                                             const float2 *s_st, float *s_w, uint32_t *s_bits, int lane) {
   const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
   const bool discover = stateful && (rp.eff == WISE_DISCOVER || rp.eff == WISE_DISCOVER_UNION);
   if constexpr (kKOnly) {
@@ -565,19 +565,42 @@ __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan
       o[i] = err ? __builtin_nanf("") : a / L;
     }
   }
-  // Selection and the new support words (lane w holds word w; a unit has at
-  // most 64 blocks, so two words).  A union row ORs into the words its plan
-  // loaded (no other unit writes them).
+  // Selection and the new support words (lane w holds word w: a unit has at
+  // most MAXB blocks, so MAXB / 32 words).  A union row ORs into the words
+  // its plan loaded (no other unit writes them).
   const bool select = discover && !err;
   int selected = 0;
   uint32_t nw = 0u;
   if (select) {
-    const float2 st = lane < nb ? s_st[lane] : make_float2(0.0f, 0.0f);
-    unsigned long long mask = 0ull;
-    const int K = nb <= 16   ? sel::select_eta_mask<16>(st, p.eta, nb, M, L, lane, mask)
-                  : nb <= 32 ? sel::select_eta_mask<32>(st, p.eta, nb, M, L, lane, mask)
-                             : sel::select_eta_mask<64>(st, p.eta, nb, M, L, lane, mask);
-    nw = lane == 0 ? static_cast<uint32_t>(mask) : lane == 1 ? static_cast<uint32_t>(mask >> 32) : 0u;
+    int K = 0;
+    if (nb <= 64) {
+      // one block per lane; the selected set comes back as a register mask
+      const float2 st = lane < nb ? s_st[lane] : make_float2(0.0f, 0.0f);
+      unsigned long long mask = 0ull;
+      K = nb <= 16   ? sel::select_eta_mask<16>(st, p.eta, nb, M, L, lane, mask)
+          : nb <= 32 ? sel::select_eta_mask<32>(st, p.eta, nb, M, L, lane, mask)
+                     : sel::select_eta_mask<64>(st, p.eta, nb, M, L, lane, mask);
+      nw = lane == 0 ? static_cast<uint32_t>(mask) : lane == 1 ? static_cast<uint32_t>(mask >> 32) : 0u;
+    } else if constexpr (MAXB > 64) {
+      // two or four blocks per lane (lane l holds blocks l*KPL ..); the
+      // selected blocks' bits are ORed into LDS words
+      static_assert(MAXB <= 256, "a long fused unit has at most 256 blocks");
+      if (lane < MAXB / 32) s_bits[lane] = 0u;
+      sel::wave_lds_sync();
+      if (nb <= 128) {
+        float2 st[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) st[j] = 2 * lane + j < nb ? s_st[2 * lane + j] : make_float2(0.0f, 0.0f);
+        K = sel::select_eta<2, 128>(st, p.eta, nb, M, L, lane, s_bits);
+      } else {
+        float2 st[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[j] = 4 * lane + j < nb ? s_st[4 * lane + j] : make_float2(0.0f, 0.0f);
+        K = sel::select_eta<4, 256>(st, p.eta, nb, M, L, lane, s_bits);
+      }
+      sel::wave_lds_sync();
+      nw = lane < MAXB / 32 ? s_bits[lane] : 0u;
+    }
     selected = rp.eff == WISE_DISCOVER ? K : sel::wave_sum_int(__popc(nw & ~rp.word));
   }
   // A discovery row's arrival goes out before the stores below, which then
@@ -627,14 +650,18 @@ __device__ __forceinline__ void finish_fused(const SplitParams &p, const RowPlan
   }
 }
 
-template <bool kBf16, int D, int W, bool kKOnly>
+// MAXB: the most blocks a unit of the launch has (64, or 256 for contexts up
+// to 8K); a wave's share of a unit is at most ceil(MAXB / W) list entries.
+template <bool kBf16, int D, int W, bool kKOnly, int MAXB>
 __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p) {
-  static_assert(W * kMaxTilesPerItem >= kMaxFusedBlocks, "tile stats of a fused unit must fit");
-  __shared__ int s_tiles[W][kMaxTilesPerItem];
+  constexpr int kTiles = (MAXB + W - 1) / W > kMaxTilesPerItem ? (MAXB + W - 1) / W : kMaxTilesPerItem;
+  static_assert(kTiles <= 64, "one lane per list entry of an item");
+  __shared__ int s_tiles[W][kTiles];
   __shared__ float s_acc[W * D];
   __shared__ float2 s_ml[W];
-  __shared__ float2 s_st[W * kMaxTilesPerItem];
+  __shared__ float2 s_st[MAXB];
   __shared__ float s_w[W];
+  __shared__ uint32_t s_bits[MAXB / 32];
   const int lane = threadIdx.x & 63;
   const int k = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);  // item slot
   const int u = blockIdx.x;  // unit = (row, head); units of a row spread over the XCDs
@@ -659,7 +686,7 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   if (k < items)
     run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], T, &lds);
   __syncthreads();  // every wave of the workgroup reaches this once
-  if (k == 0) finish_fused<D, kKOnly>(p, rp, u, h, nb, items, s_acc, s_ml, s_st, s_w, lane);
+  if (k == 0) finish_fused<D, kKOnly, MAXB>(p, rp, u, h, nb, items, s_acc, s_ml, s_st, s_w, s_bits, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -873,6 +900,42 @@ static hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t stre
   return hipGetLastError();
 }
 
+// One workgroup per unit, p.fused_waves waves; units of up to 64 blocks use
+// the short shape (one block per lane in the selection), longer ones the
+// long shape.
+template <bool kBf16, int D, bool kKOnly, int MAXB>
+static hipError_t launch_fused_w(const SplitParams &p, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
+  const dim3 units(static_cast<unsigned>(p.rows) * p.heads);
+  switch (p.fused_waves) {
+    case 4:
+      if constexpr (MAXB <= 64)
+        return launch_timed(split_fused_kernel<kBf16, D, 4, kKOnly, MAXB>, units, dim3(64 * 4), stream, ev_begin,
+                            ev_end, p);
+      break;
+    case 8:
+      return launch_timed(split_fused_kernel<kBf16, D, 8, kKOnly, MAXB>, units, dim3(64 * 8), stream, ev_begin,
+                          ev_end, p);
+    case 16:
+      // fp32 at head_dim 128 needs more than the 128 registers a 16-wave workgroup allows
+      if constexpr (kBf16 || D == 64)
+        return launch_timed(split_fused_kernel<kBf16, D, 16, kKOnly, MAXB>, units, dim3(64 * 16), stream,
+                            ev_begin, ev_end, p);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool kBf16, int D>
+static hipError_t launch_fused(const SplitParams &p, bool k_only, hipEvent_t ev_begin, hipEvent_t ev_end,
+                               hipStream_t stream) {
+  const bool wide = p.max_blocks > kMaxFusedBlocks;
+  if (k_only)
+    return wide ? launch_fused_w<kBf16, D, true, kWideFusedBlocks>(p, ev_begin, ev_end, stream)
+                : launch_fused_w<kBf16, D, true, kMaxFusedBlocks>(p, ev_begin, ev_end, stream);
+  return wide ? launch_fused_w<kBf16, D, false, kWideFusedBlocks>(p, ev_begin, ev_end, stream)
+              : launch_fused_w<kBf16, D, false, kMaxFusedBlocks>(p, ev_begin, ev_end, stream);
+}
+
 template <bool kBf16, int D>
 static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, bool fused, int cus,
                                hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
@@ -888,28 +951,7 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, b
     if (e != hipSuccess) return e;
     return launch_timed(split_listed_kernel<kBf16, D>, dim3(groups), block, stream, ev_begin, ev_end, p);
   }
-  if (fused) {
-    // one workgroup per unit, one wave per item slot
-    const dim3 units(static_cast<unsigned>(p.rows) * p.heads);
-    if (k_only) {
-      if (p.items_per_unit <= 4)
-        return launch_timed(split_fused_kernel<kBf16, D, 4, true>, units, dim3(64 * 4), stream, ev_begin, ev_end, p);
-      if (p.items_per_unit <= 8)
-        return launch_timed(split_fused_kernel<kBf16, D, 8, true>, units, dim3(64 * 8), stream, ev_begin, ev_end, p);
-      if constexpr (kBf16 || D == 64)
-        return launch_timed(split_fused_kernel<kBf16, D, 16, true>, units, dim3(64 * 16), stream, ev_begin, ev_end,
-                            p);
-      return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
-    }
-    if (p.items_per_unit <= 4)
-      return launch_timed(split_fused_kernel<kBf16, D, 4, false>, units, dim3(64 * 4), stream, ev_begin, ev_end, p);
-    if (p.items_per_unit <= 8)
-      return launch_timed(split_fused_kernel<kBf16, D, 8, false>, units, dim3(64 * 8), stream, ev_begin, ev_end, p);
-    if constexpr (kBf16 || D == 64)
-      return launch_timed(split_fused_kernel<kBf16, D, 16, false>, units, dim3(64 * 16), stream, ev_begin, ev_end,
-                          p);
-    return hipErrorInvalidValue;  // fp32 at head_dim 128 fuses at most 8 items
-  }
+  if (fused) return launch_fused<kBf16, D>(p, k_only, ev_begin, ev_end, stream);
   const dim3 grid(static_cast<unsigned>(p.rows) * p.heads * p.chunk_groups);
   if (k_only) return launch_timed(split_static_kernel<kBf16, D, true>, grid, block, stream, ev_begin, ev_end, p);
   return launch_timed(split_static_kernel<kBf16, D, false>, grid, block, stream, ev_begin, ev_end, p);
@@ -918,7 +960,7 @@ static hipError_t launch_typed(const SplitParams &p, bool listed, bool k_only, b
 hipError_t launch_split(const SplitParams &p, int dtype, int head_dim, bool listed, bool k_only, bool fused,
                         int cus, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
   if (listed && (k_only || fused)) return hipErrorInvalidValue;  // K-only and fused calls use the static grid
-  if (fused && (p.items_per_unit > kMaxFusedItems || p.max_blocks > kMaxFusedBlocks || (k_only && !p.lse)))
+  if (fused && (p.fused_waves < 1 || p.max_blocks > kWideFusedBlocks || (k_only && !p.lse)))
     return hipErrorInvalidValue;
   if (dtype == WISE_BF16 && head_dim == 128)
     return launch_typed<true, 128>(p, listed, k_only, fused, cus, ev_begin, ev_end, stream);

@@ -200,15 +200,13 @@ wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
  * the counters ("What changes", first bullet: the finish kernel; "Summary":
  * B = 32 blocks and the eta = 0.95 rule; the author's reply on density: the
  * selected and causal block counts).  `a` and `s` must describe the same call as the decode
- * call (s == NULL after wise_decode_dense).  When every (row, head)'s work
- * items fit one split workgroup the decode call has already done all of
- * this in the same kernel, and this call only validates its arguments:
- * with heads <= 255, every call with max_ctx <= 1024, and small launches
- * (fewer than 1024 eight-tile items over all rows and heads) with max_ctx
- * <= 2048; for fp32 at head_dim 128 only launches of at least 1024 such
- * items with max_ctx <= 1024, and small ones with max_ctx <= 256.  It is
- * still required: which shapes finish inside the decode kernel is the
- * library's choice and may change. */
+ * call (s == NULL after wise_decode_dense).  When the decode call gives each
+ * (row, head) one workgroup, it has already done all of this in the same
+ * kernel, and this call only validates its arguments: with heads <= 255,
+ * every call with max_ctx <= 8192, except plain dense calls (s == NULL) of
+ * fewer than 512 (row, head) pairs with max_ctx > 1024 (or > 2048 for small
+ * launches of short rows).  It is still required: which shapes finish
+ * inside the decode kernel is the library's choice and may change. */
 wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws,
                                size_t ws_bytes, void *stream);
 

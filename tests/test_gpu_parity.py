@@ -191,20 +191,21 @@ def test_head_counts(torch, heads, ctxs):
     run_schedule(w)
 
 
-@pytest.mark.parametrize("rows,heads,tiles,dtype,d", [(32, 16, 16, "bf16", 128), (32, 32, 32, "bf16", 128),
-                                                   (16, 32, 16, "f32", 64)])
+@pytest.mark.parametrize("rows,heads,tiles,dtype,d", [(8, 16, 16, "bf16", 128), (16, 16, 32, "bf16", 128),
+                                                   (8, 16, 16, "f32", 64)])
 def test_long_items(torch, rows, heads, tiles, dtype, d):
-    """Calls with no sparse rows whose launch stays large run 16- or 32-tile
-    items on the static grid (a quarter or half of the partials); sampled rows
-    of every depth -- dense, discover, union, and the sparse depth on the
-    listed grid -- against the oracle.  The same dense rows in a call with a
-    per-row mode array (the listed grid, whose plan kernel picks the item
-    length from the same tiles) are bitwise the dense call's."""
+    """Calls with no sparse rows whose units outgrow the fused kernel (16K
+    tokens) and whose launch stays large run 16- or 32-tile items on the
+    static grid (a quarter or half of the partials); every row of every
+    depth -- dense, discover, union, and the sparse depth on the listed grid
+    -- against the oracle.  The same dense rows in a call with a per-row mode
+    array (the listed grid, whose plan kernel picks the item length from the
+    same tiles) are bitwise the dense call's."""
     w = synth.Workload(name=f"long{tiles}_{rows}x{heads}_{dtype}{d}", rows=rows, heads=heads, head_dim=d, dtype=dtype,
-                       page_size=16, shuffle=True, alpha=2.5, seed=93, ctx=4096, hot=6,
+                       page_size=16, shuffle=True, alpha=2.5, seed=93, ctx=16384, hot=6,
                        schedule=(W.WISE_DENSE, W.WISE_DISCOVER, W.WISE_DISCOVER_UNION, W.WISE_SPARSE))
-    units = rows * heads
-    assert units * (128 // tiles) >= 4096 and (tiles == 32 or units * (128 // 32) < 4096)
+    units, nb = rows * heads, 16384 // 32
+    assert units * (nb // tiles) >= 4096 and (tiles == 32 or units * (nb // 32) < 4096)
     reps, state = run_schedule(w, pool=True)
     assert all(r.counters[W.CTR_FALLBACKS] == 0 and r.counters[W.CTR_ERRORS] == 0 for r in reps)
     li, dev = _one_layer(w, 0)
@@ -219,10 +220,10 @@ def test_long_items(torch, rows, heads, tiles, dtype, d):
     assert torch.equal(dev.out, long_out)
 
 
-@pytest.mark.parametrize("rows,heads,ctx,tiles", [(64, 16, 4096, 32), (32, 16, 4096, 16), (8, 16, 4096, 8),
-                                                  (16, 16, 8192, 16)])
+@pytest.mark.parametrize("rows,heads,ctx,tiles", [(32, 16, 16384, 32), (12, 16, 16384, 16), (2, 16, 16384, 8)])
 def test_listed_long_items(torch, rows, heads, ctx, tiles):
-    """Calls with sparse rows take their item length in the plan kernel from
+    """Calls whose units outgrow the fused kernel (16K tokens) and that have
+    sparse rows take their item length in the plan kernel from
     the tiles they attend, by the rule dense calls take on the host: 32 tiles
     when the launch keeps at least 4096 items of 32, else 16 on that
     condition, else 8.  With every block selected the attended tiles are the
@@ -261,12 +262,14 @@ def test_listed_long_items(torch, rows, heads, ctx, tiles):
 
 
 def test_plan_many_units(torch):
-    """More than 4096 units: the plan kernel's threads take five units each,
-    the fifth keeping its tile count in the workspace between the passes
-    (the first four stay in registers).  Discovery, then a sparse and a
-    mixed call (32-tile items, full-length items listed before the short
-    last ones); every row against the oracle, counters exact."""
-    w = synth.Workload(name="plan_many_units", rows=260, heads=16, head_dim=64, dtype="bf16", page_size=16,
+    """More than 4096 units (rows of 256 heads, more than the fused kernel's
+    8-bit arrival count holds, take the plan kernel): the plan kernel's
+    threads take five units each, the fifth keeping its tile count in the
+    workspace between the passes (the first four stay in registers).
+    Discovery, then a sparse and a mixed call (full-length items listed
+    before the short last ones); every row against the oracle, counters
+    exact."""
+    w = synth.Workload(name="plan_many_units", rows=17, heads=256, head_dim=64, dtype="bf16", page_size=16,
                        shuffle=True, alpha=4.0, seed=97, ctx=1100, hot=6, schedule=(W.WISE_DISCOVER,))
     assert w.rows * w.heads > 4 * 1024
     say(f"[{w.name}] {w.rows * w.heads} units: discover, sparse, mixed")
@@ -279,7 +282,7 @@ def test_plan_many_units(torch):
     # every plan thread's units 5t .. 5t + 4 span several rows
     rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_SPARSE, required=1, pool=True)
     say(f"   sparse: max_abs {rep.max_abs:.2e}")
-    modes = np.array([W.WISE_SPARSE, W.WISE_DENSE, W.WISE_SPARSE, W.WISE_DISCOVER_UNION] * (w.rows // 4),
+    modes = np.array(([W.WISE_SPARSE, W.WISE_DENSE, W.WISE_SPARSE, W.WISE_DISCOVER_UNION] * w.rows)[:w.rows],
                      dtype=np.uint8)
     ctr0 = st.counters.cpu().numpy().copy()
     rep = check_call(w, li1, dev1, ws, st, mode=W.WISE_SPARSE, row_modes=modes, required=1, pool=True)
