@@ -373,7 +373,7 @@ def replay_ms(graphs, n, warmup, torch):
 
 
 def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=None, headline=False,
-            args=None):
+            args=None, dense_reference=True):
     """Everything measured on one workload; returns (entry, extras) where
     extras holds what only the headline line reports."""
     import torch
@@ -452,7 +452,8 @@ def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=No
     for name in kinds:
         pcs = [pc for rep in range(plan.replicas) for pc, key in plan.calls[rep] if key[0] == name]
         groups.append((name, pcs))
-    groups.append(("dense_same_kv", dense_pcs))
+    if dense_reference:
+        groups.append(("dense_same_kv", dense_pcs))
     dense_bytes = split_bytes(w, plan.ctx, np.full(w.rows, W.WISE_DENSE), None)
     if graphs:
         for name, pcs in groups:
@@ -472,27 +473,28 @@ def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=No
             out[name].update({"call_us": round(call_us, 2), "call_GBps": round(mb * 1e6 / (call_us * 1e-6) / 1e9, 1),
                               "call_frac": round(mb * 1e6 / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     # split-stamped dense reference, rotating over every KV set of the run
-    n_it = max(16, 2 * len(dense_pcs))
+    n_it = max(16, 2 * len(dense_pcs)) if dense_reference else 0
     ev2 = harness.HipEvents(2 * n_it)
     for it in range(n_it):
         pc = dense_pcs[it % len(dense_pcs)]
         pc.set_events(ev2.handle(2 * it), ev2.handle(2 * it + 1))
         pc.run(sh)
     torch.cuda.synchronize()
-    dms = float(np.mean([ev2.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]))
     for pc in dense_pcs:
         pc.set_events(None, None)
-    out.setdefault("dense_same_kv", {"algorithmic_MB": round(dense_bytes / 1e6, 3)})
-    out["dense_same_kv"].update({"split_us": round(dms * 1e3, 2),
-                                 "split_GBps": round(dense_bytes / (dms * 1e-3) / 1e9, 1)})
+    if dense_reference:
+        dms = float(np.mean([ev2.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]))
+        out.setdefault("dense_same_kv", {"algorithmic_MB": round(dense_bytes / 1e6, 3)})
+        out["dense_same_kv"].update({"split_us": round(dms * 1e3, 2),
+                                     "split_GBps": round(dense_bytes / (dms * 1e-3) / 1e9, 1)})
     reuse = "mixed" if plan.mixed else ("sparse" if "sparse" in out else None)
-    if reuse:
+    if reuse and dense_reference:
         out[reuse]["speedup_vs_dense_split"] = round(out["dense_same_kv"]["split_us"] / out[reuse]["split_us"], 3)
         if "call_us" in out[reuse]:
             out[reuse]["speedup_vs_dense_call"] = round(out["dense_same_kv"]["call_us"] / out[reuse]["call_us"], 3)
 
     # ---- read ceiling: a pure gather of the same K/V pages in items of the same length ----
-    if probe is not None and reuse:
+    if probe is not None and reuse and dense_reference:
         e = 2 if w.dtype == "bf16" else 4
         fused = (w.max_ctx + 31) // 32 <= 32
         ceil = {}
@@ -693,6 +695,8 @@ def main():
                     help="workloads measured per call in the contexts block ('' for none)")
     ap.add_argument("--context-steps", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-reference", action="store_true",
+                    help="skip the dense calls on the same KV (counter runs of the headline's own launches)")
     ap.add_argument("--no-read-ceiling", action="store_true")
     ap.add_argument("--no-lse-route", action="store_true")
     ap.add_argument("--no-page-route", action="store_true")
@@ -740,7 +744,7 @@ def main():
     log(f"headline workload {w.name}")
     head, ex = measure(w, dev, steps=args.steps, warmup=args.warmup,
                        replicas=args.replicas or default_replicas(w), kv_layers=args.kv_layers, graphs=graphs,
-                       probe=probe, headline=True, args=args)
+                       probe=probe, headline=True, args=args, dense_reference=not args.no_dense_reference)
     plan = ex["plan"]
     rows_per_step = w.rows * ex["calls"]
     achieved = ex["achieved"]   # every timed split launch's algorithmic bytes / its stamped duration

@@ -41,13 +41,54 @@ def split_source_digest() -> str:
     return h.hexdigest()
 
 
+def k_only_kernel(name: str) -> bool:
+    """A K-only (LSE route) instantiation: split_static_kernel<bf16, D, K-only>
+    or split_fused_kernel<bf16, D, waves, K-only, max blocks>."""
+    m = re.search(r"split_(static|fused)_kernel<([^>]*)>", name)
+    if not m:
+        return False
+    args = [a.strip() for a in m.group(2).split(",")]
+    pos = 2 if m.group(1) == "static" else 3
+    return len(args) > pos and args[pos] == "true"
+
+
 def short(name: str) -> str:
     for key in ("split_fused_kernel", "split_static_kernel", "split_listed_kernel", "plan_kernel", "finish_kernel",
-                "compact_pages_kernel", "snapshot_kernel", "restore_kernel"):
+                "compact_pages_kernel", "snapshot_kernel", "restore_kernel", "read_probe_kernel"):
         if key in name:
             tmpl = name[name.find("<"): name.find(">") + 1] if "<" in name else ""
             return key + tmpl
     return name if len(name) < 70 else name[:67] + "..."
+
+
+def duration_groups(trace_csv: str, min_share: float = 0.02):
+    """Per kernel, its dispatch durations split into groups wherever the
+    sorted durations jump by more than 15% (one kernel serves calls of very
+    different sizes: a sparse call and a dense one of the same launch
+    shape): [(kernel, [(dispatches, mean us, min us, max us), ...])] for the
+    kernels holding at least min_share of the traced time."""
+    durs = {}
+    for r in csv.DictReader(open(trace_csv)):
+        if r.get("Kind", "KERNEL_DISPATCH") != "KERNEL_DISPATCH":
+            continue
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        durs.setdefault(r["Kernel_Name"], []).append(d)
+    total = sum(sum(v) for v in durs.values()) or 1.0
+    out = []
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        if sum(v) / total < min_share:
+            continue
+        v = sorted(v)
+        groups, cur = [], [v[0]]
+        for x in v[1:]:
+            if x > cur[-1] * 1.15:
+                groups.append(cur)
+                cur = [x]
+            else:
+                cur.append(x)
+        groups.append(cur)
+        out.append((name, [(len(g), sum(g) / len(g), g[0], g[-1]) for g in groups]))
+    return out
 
 
 def kernel_stats(stats_csv: str, out_md: str, command: str) -> None:
@@ -60,6 +101,14 @@ def kernel_stats(stats_csv: str, out_md: str, command: str) -> None:
     for r in rows:
         lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    if os.path.exists(trace_csv):
+        lines += ["", "Dispatch durations of the main kernels, grouped where the sorted durations jump by",
+                  "more than 15% (calls of different sizes on the same kernel):", "",
+                  "| kernel | dispatches | mean (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+        for name, groups in duration_groups(trace_csv):
+            for n, mean, lo, hi in groups:
+                lines.append(f"| {short(name)} | {n} | {mean:.2f} | {lo:.2f} | {hi:.2f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -83,9 +132,8 @@ def traffic(fetch_csv: str, write_csv: str, out_md: str, workload: str, mib: int
         raise SystemExit("calibration kernel not found in the counter output")
     scale_f = known / max(cal_f[0])
     scale_w = known / max(cal_w[0])
-    # the decode split kernel (the K-only instantiation of the LSE route is not counted)
-    split = [k for k in f if "split_" in k and "kernel" in k
-             and not re.search(r"split_(static|fused)_kernel<[^>]*, true>", k)]
+    # the decode split kernel (the K-only instantiations of the LSE route are not counted)
+    split = [k for k in f if "split_" in k and "kernel" in k and not k_only_kernel(k)]
     fk = [x for k in split for x in f[k]]
     wk = [x for k in split for x in w.get(k, [])]
     fetch_kib = sum(fk) / len(fk)
