@@ -220,7 +220,7 @@ class ReadProbe:
         self.L.wise_read_probe.restype = ctypes.c_int
 
     @staticmethod
-    def items_for(w, ctx, eff_modes, support_words, fused_units):
+    def items_for(w, ctx, eff_modes, support_words, fused_units, k_only=False):
         """(items [n, 4] int32, tiles int32, K/V bytes) of one call: every
         (row, head)'s attended blocks cut into items as the library cuts
         them -- a unit's tiles spread over four waves when the call finishes
@@ -242,7 +242,7 @@ class ReadProbe:
         for (r, h, blocks), c in zip(lists, counts):
             n = int(ctx[r])
             toks = np.minimum(32, n - 32 * blocks)
-            nbytes += int(2 * toks.sum() * w.head_dim * e)
+            nbytes += int((1 if k_only else 2) * toks.sum() * w.head_dim * e)
             t = max(1, -(-c // 4)) if fused_units else T
             assert t <= 64 and (len(blocks) == 0 or (blocks.min() >= 0 and 32 * blocks.max() < n))
             for i in range(0, c, t):
@@ -590,10 +590,34 @@ def headline_legs(w, plan, dev, sh, steps, warmup, args, out, graphs):
         torch.cuda.synchronize()
         sms = float(np.mean([ev3.elapsed_ms(2 * it, 2 * it + 1) for it in range(n_it)]))
         lbytes = split_bytes(w, plan.ctx, np.full(w.rows, LSE_ROUTE), None)
+        ceiling = None
+        if not args.no_read_ceiling:
+            # a pure gather of the same K pages in items of the same length (K only)
+            probe = ReadProbe()
+            e = 2 if w.dtype == "bf16" else 4
+            fused = (w.max_ctx + 31) // 32 <= 32
+            launches, keep, kb = [], [], 0
+            for layer_dev in plan.kv.values():
+                items, tiles, kb = ReadProbe.items_for(w, plan.ctx, np.full(w.rows, W.WISE_DENSE), None, fused,
+                                                       k_only=True)
+                it_d, ti_d = torch.from_numpy(items).to(dev), torch.from_numpy(tiles).to(dev)
+                sink = torch.empty(len(items), dtype=torch.int32, device=dev)
+                keep += [it_d, ti_d, sink]
+                sp, sh_, st_, _ = layer_dev.k.stride()
+                launches.append((layer_dev.k.data_ptr(), None, sp * e, sh_ * e, st_ * e, w.head_dim * e,
+                                 layer_dev.block_table.data_ptr(), layer_dev.block_table.stride(0),
+                                 layer_dev.ctx_len.data_ptr(), int(math.log2(w.page_size)), it_d.data_ptr(),
+                                 ti_d.data_ptr(), len(items), sink.data_ptr()))
+            n_p = max(16, 2 * len(launches))
+            evp = harness.HipEvents(2 * n_p)
+            probe.time(launches, sh, min(4, len(launches)), evp)
+            pms = probe.time(launches, sh, n_p, evp)
+            ceiling = {"us": round(pms * 1e3, 2), "k_MB": round(kb / 1e6, 3), "GBps": round(kb / (pms * 1e-3) / 1e9, 1)}
         res["lse_discover"] = {"split_us": round(sms * 1e3, 2),
                                "call_us_eager": round(ev3.elapsed_ms(2 * n_it, 2 * n_it + 1) / n_it * 1e3, 2),
                                "algorithmic_MB": round(lbytes / 1e6, 3),
                                "split_GBps": round(lbytes / (sms * 1e-3) / 1e9, 1),
+                               "read_ceiling_k_only": ceiling,
                                "note": "K-only split + LSE selection, eager back-to-back calls"}
         for a, _ in sets:
             a.ev_split_begin = a.ev_split_end = None

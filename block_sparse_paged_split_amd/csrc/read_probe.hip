@@ -6,8 +6,9 @@
 // them into one XOR word per wave so that no load is dead.  The item list
 // (row, head, offset into a tile list, tile count) is built on the host from
 // the same supports and contexts the attention call reads, so the probe
-// moves the call's K/V bytes in items of the same length.  It is not part of
-// the attention library; only the benchmark loads it.
+// moves the call's K/V bytes in items of the same length.  With no V cache
+// it reads K only (the LSE route's pass).  It is not part of the attention
+// library; only the benchmark loads it.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const ProbeParams p) {
   const int n = p.ctx_len[r];
   const int c = lane % LPT, g = lane / LPT;
   const char *kh = p.k + h * p.stride_head_b + c * 16 + g * p.stride_token_b;
-  const char *vh = p.v + h * p.stride_head_b + c * 16 + g * p.stride_token_b;
+  const char *vh = p.v ? p.v + h * p.stride_head_b + c * 16 + g * p.stride_token_b : nullptr;
   const int32_t *bt = p.block_table + r * p.bt_stride;
   const int pmask = (1 << p.page_shift) - 1;
   u32x4 acc = {0u, 0u, 0u, 0u};
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const ProbeParams p) {
       const int64_t off = static_cast<int64_t>(page) * p.stride_page_b + (t0 & pmask) * p.stride_token_b;
       const bool valid = t0 + g < n;
       kr[j] = valid ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kh + off)) : u32x4{0u, 0u, 0u, 0u};
-      vr[j] = valid ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vh + off)) : u32x4{0u, 0u, 0u, 0u};
+      vr[j] = (valid && p.v) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vh + off))
+                             : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc ^= kr[j] ^ vr[j];

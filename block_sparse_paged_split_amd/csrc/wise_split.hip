@@ -513,16 +513,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
 // items leave their partials and tile stats in LDS, and two waves then finish
 // the unit side by side.  Wave 0 merges the partials into the output exactly
 // as the finish kernel would (the same merge in the same order, so the
-// output bits do not depend on which kernel ran it) and does the row's
-// bookkeeping; wave 1 runs the eta selection and writes or ORs the support.
-// Both compute the row's (M, L) by the same operations, so they agree bit
-// for bit.  A discovery row's tag and causal-block count are updated by the
-// last of its heads to arrive, counted in the tag's reserved word (arrivals
-// | error heads << 8), which that last arrival returns to zero; each head
-// adds the blocks it newly selected to the density counter itself, so the
-// arrival does not wait for the selection.  Every unit of the row planned
-// from the tag before any head arrives, so the update cannot race with a
-// plan.
+// output bits do not depend on which kernel ran it); wave 1 runs the eta
+// selection, writes or ORs the support and does the row's bookkeeping.  Both
+// compute the unit's (M, L) by the same operations, so they agree bit for
+// bit.  A discovery row's tag and density counters are updated by the last
+// of its heads to arrive, counted in the tag's reserved word (arrivals |
+// error heads << 8 | newly selected blocks << 16), which that last arrival
+// returns to zero.  Every unit of the row planned from the tag before any
+// head arrives, so the update cannot race with a plan.
 // ---------------------------------------------------------------------------
 // (M, L) of a unit from its items' partials in LDS: M = max m_i, L = sum
 // l_i 2^(m_i - M) (or M = the external LSE in base-2 units and L = 1 on the
@@ -550,33 +548,15 @@ __device__ __forceinline__ void unit_norm(const SplitParams &p, int u, int items
   }
 }
 
-// Wave 0: output, error count, and the row's arrival and bookkeeping.
+// Wave 0: the output (NaN for a unit with bad data) and its error count.
+// The LSE route writes no output; wave 1 counts its errors.
 template <int D, bool kKOnly>
-__device__ __forceinline__ void finish_output(const SplitParams &p, const RowPlan &rp, int u, int h, int nb,
-                                              int items, const float *s_acc, const float2 *s_ml, float *s_w,
-                                              int lane) {
-  const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
-  const bool discover = stateful && (rp.eff == WISE_DISCOVER || rp.eff == WISE_DISCOVER_UNION);
-  if constexpr (kKOnly) {
-    // LSE route: a row whose union window broke did no work; its tag is invalidated
-    if (!discover && !rp.bad) {
-      if (stateful && rp.req == WISE_DISCOVER_UNION && h == 0 && lane == 0)
-        p.tags[static_cast<int64_t>(rp.slot) * p.layers + p.layer].discoveries = 0;
-      return;
-    }
-  }
-  float M, L;
-  bool err;
-  unit_norm<kKOnly>(p, u, items, s_ml, s_w, lane, M, L, err);
-  // the row's arrival goes out first; the output stores overlap its round trip
-  wise_tag *tag = stateful ? p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer : nullptr;
-  unsigned int *arrive = discover ? reinterpret_cast<unsigned int *>(&tag->reserved) : nullptr;
-  unsigned int all = 0u;
-  if (discover && lane == 0) {
-    const unsigned int mine = 1u | (err ? 1u << 8 : 0u);
-    all = atomicAdd(arrive, mine) + mine;
-  }
+__device__ __forceinline__ void finish_output(const SplitParams &p, int u, int items, const float *s_acc,
+                                              const float2 *s_ml, float *s_w, int lane) {
   if constexpr (!kKOnly) {
+    float M, L;
+    bool err;
+    unit_norm<kKOnly>(p, u, items, s_ml, s_w, lane, M, L, err);
     sel::wave_lds_sync();
     constexpr int kOut = D / 64;  // output elements per lane
 #pragma unroll
@@ -586,20 +566,89 @@ __device__ __forceinline__ void finish_output(const SplitParams &p, const RowPla
       for (int t = 0; t < items; ++t) a = fmaf(s_acc[t * D + dd], s_w[t], a);
       p.out[static_cast<int64_t>(u) * D + dd] = err ? __builtin_nanf("") : a / L;
     }
+    if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
   }
-  if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
-  if (!stateful || lane != 0) return;
+}
+
+// Wave 1: the eta selection of a discovery unit, the support words written
+// (DISCOVER) or ORed (DISCOVER_UNION; into the words its plan loaded -- no
+// other unit writes them), the row's arrival and, for its last head, the tag
+// and the density counters.
+template <bool kKOnly, int MAXB>
+__device__ __forceinline__ void finish_row(const SplitParams &p, const RowPlan &rp, int u, int h, int nb, int items,
+                                           const float2 *s_ml, const float2 *s_st, uint32_t *s_bits, int lane) {
+  const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
+  const bool discover = stateful && (rp.eff == WISE_DISCOVER || rp.eff == WISE_DISCOVER_UNION);
+  wise_tag *tag = stateful ? p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer : nullptr;
   if (!discover) {
-    // a union row whose discovery window is broken ran dense: the rest of
-    // this token runs dense too
-    if (rp.req == WISE_DISCOVER_UNION && h == 0) tag->discoveries = 0;
-    return;
+    // a union row whose discovery window is broken ran dense (on the LSE
+    // route it did no work): the rest of this token runs dense too
+    if (stateful && rp.req == WISE_DISCOVER_UNION && h == 0 && lane == 0) tag->discoveries = 0;
+    if (!kKOnly || !rp.bad) return;
   }
-  if (static_cast<int>(all & 0xFFu) != p.heads) return;
+  float M, L;
+  bool err;
+  unit_norm<kKOnly>(p, u, items, s_ml, nullptr, lane, M, L, err);
+  if constexpr (kKOnly) {
+    if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
+    if (!discover) return;
+  }
+  int K = 0;
+  uint32_t nw = 0u;  // lane w: new support word w (a unit has at most MAXB / 32 words)
+  if (!err) {
+    if (nb <= 64) {
+      // one block per lane; the selected set comes back as a register mask
+      const float2 st = lane < nb ? s_st[lane] : make_float2(0.0f, 0.0f);
+      unsigned long long mask = 0ull;
+      K = nb <= 16   ? sel::select_eta_mask<16>(st, p.eta, nb, M, L, lane, mask)
+          : nb <= 32 ? sel::select_eta_mask<32>(st, p.eta, nb, M, L, lane, mask)
+                     : sel::select_eta_mask<64>(st, p.eta, nb, M, L, lane, mask);
+      nw = lane == 0 ? static_cast<uint32_t>(mask) : lane == 1 ? static_cast<uint32_t>(mask >> 32) : 0u;
+    } else if constexpr (MAXB > 64) {
+      // two or four blocks per lane (lane l holds blocks l*KPL ..); the
+      // selected blocks' bits are ORed into LDS words
+      static_assert(MAXB <= 256, "a long fused unit has at most 256 blocks");
+      if (lane < MAXB / 32) s_bits[lane] = 0u;
+      sel::wave_lds_sync();
+      if (nb <= 128) {
+        float2 st[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) st[j] = 2 * lane + j < nb ? s_st[2 * lane + j] : make_float2(0.0f, 0.0f);
+        K = sel::select_eta<2, 128>(st, p.eta, nb, M, L, lane, s_bits);
+      } else {
+        float2 st[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[j] = 4 * lane + j < nb ? s_st[4 * lane + j] : make_float2(0.0f, 0.0f);
+        K = sel::select_eta<4, 256>(st, p.eta, nb, M, L, lane, s_bits);
+      }
+      sel::wave_lds_sync();
+      nw = lane < MAXB / 32 ? s_bits[lane] : 0u;
+    }
+  }
+  const int selected = err ? 0 : rp.eff == WISE_DISCOVER ? K : sel::wave_sum_int(__popc(nw & ~rp.word));
+  // the arrival goes out before the support stores, which overlap its round trip
+  unsigned int *arrive = reinterpret_cast<unsigned int *>(&tag->reserved);
+  unsigned int all = 0u;
+  if (lane == 0) {
+    const unsigned int mine = 1u | (err ? 1u << 8 : 0u) | (static_cast<unsigned int>(selected) << 16);
+    all = atomicAdd(arrive, mine) + mine;
+  }
+  if (!err) {
+    uint32_t *sw = p.support + ((static_cast<int64_t>(rp.slot) * p.layers + p.layer) * p.heads + h) * p.words;
+    if (rp.eff == WISE_DISCOVER) {
+      for (int w = lane; w < p.words; w += 64) sw[w] = w == lane ? nw : 0u;
+    } else if (lane < p.words && (nw & ~rp.word) != 0u) {
+      sw[lane] = rp.word | nw;  // the other words keep their bits
+    }
+  }
+  if (lane != 0 || static_cast<int>(all & 0xFFu) != p.heads) return;
   atomicExch(arrive, 0u);
   const int err_heads = static_cast<int>((all >> 8) & 0xFFu);
-  if (p.counters && rp.eff == WISE_DISCOVER)
-    atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(nb) * (p.heads - err_heads));
+  if (p.counters) {
+    atomicAdd(p.counters + WISE_CTR_SELECTED, static_cast<unsigned long long>(all >> 16));
+    if (rp.eff == WISE_DISCOVER)
+      atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(nb) * (p.heads - err_heads));
+  }
   // a bad page in any head of the row breaks this discovery
   if (rp.eff == WISE_DISCOVER) {
     tag->request = p.row_request[rp.row];
@@ -609,63 +658,6 @@ __device__ __forceinline__ void finish_output(const SplitParams &p, const RowPla
     tag->discoveries = err_heads ? 0 : tag->discoveries + 1;
   }
 }
-
-// Wave 1: the eta selection of a discovery unit, the support words written
-// (DISCOVER) or ORed (DISCOVER_UNION; into the words its plan loaded -- no
-// other unit writes them), and the newly selected blocks added to the
-// density counter.
-template <bool kKOnly, int MAXB>
-__device__ __forceinline__ void finish_select(const SplitParams &p, const RowPlan &rp, int u, int h, int nb,
-                                              int items, const float2 *s_ml, const float2 *s_st, uint32_t *s_bits,
-                                              int lane) {
-  const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
-  const bool discover = stateful && (rp.eff == WISE_DISCOVER || rp.eff == WISE_DISCOVER_UNION);
-  if (!discover) return;
-  float M, L;
-  bool err;
-  unit_norm<kKOnly>(p, u, items, s_ml, nullptr, lane, M, L, err);
-  if (err) return;
-  int K = 0;
-  uint32_t nw = 0u;  // lane w: new support word w (a unit has at most MAXB / 32 words)
-  if (nb <= 64) {
-    // one block per lane; the selected set comes back as a register mask
-    const float2 st = lane < nb ? s_st[lane] : make_float2(0.0f, 0.0f);
-    unsigned long long mask = 0ull;
-    K = nb <= 16   ? sel::select_eta_mask<16>(st, p.eta, nb, M, L, lane, mask)
-        : nb <= 32 ? sel::select_eta_mask<32>(st, p.eta, nb, M, L, lane, mask)
-                   : sel::select_eta_mask<64>(st, p.eta, nb, M, L, lane, mask);
-    nw = lane == 0 ? static_cast<uint32_t>(mask) : lane == 1 ? static_cast<uint32_t>(mask >> 32) : 0u;
-  } else if constexpr (MAXB > 64) {
-    // two or four blocks per lane (lane l holds blocks l*KPL ..); the
-    // selected blocks' bits are ORed into LDS words
-    static_assert(MAXB <= 256, "a long fused unit has at most 256 blocks");
-    if (lane < MAXB / 32) s_bits[lane] = 0u;
-    sel::wave_lds_sync();
-    if (nb <= 128) {
-      float2 st[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) st[j] = 2 * lane + j < nb ? s_st[2 * lane + j] : make_float2(0.0f, 0.0f);
-      K = sel::select_eta<2, 128>(st, p.eta, nb, M, L, lane, s_bits);
-    } else {
-      float2 st[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st[j] = 4 * lane + j < nb ? s_st[4 * lane + j] : make_float2(0.0f, 0.0f);
-      K = sel::select_eta<4, 256>(st, p.eta, nb, M, L, lane, s_bits);
-    }
-    sel::wave_lds_sync();
-    nw = lane < MAXB / 32 ? s_bits[lane] : 0u;
-  }
-  const int selected = rp.eff == WISE_DISCOVER ? K : sel::wave_sum_int(__popc(nw & ~rp.word));
-  uint32_t *sw = p.support + ((static_cast<int64_t>(rp.slot) * p.layers + p.layer) * p.heads + h) * p.words;
-  if (rp.eff == WISE_DISCOVER) {
-    for (int w = lane; w < p.words; w += 64) sw[w] = w == lane ? nw : 0u;
-  } else if (lane < p.words && (nw & ~rp.word) != 0u) {
-    sw[lane] = rp.word | nw;  // the other words keep their bits
-  }
-  if (lane == 0 && p.counters && selected > 0)
-    atomicAdd(p.counters + WISE_CTR_SELECTED, static_cast<unsigned long long>(selected));
-}
-
 
 // MAXB: the most blocks a unit of the launch has (64, or 256 for contexts up
 // to 8K); a wave's share of a unit is at most ceil(MAXB / W) list entries.
@@ -704,8 +696,8 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   if (k < items)
     run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], T, &lds);
   __syncthreads();  // every wave of the workgroup reaches this once
-  if (k == 0) finish_output<D, kKOnly>(p, rp, u, h, nb, items, s_acc, s_ml, s_w, lane);
-  if (k == 1) finish_select<kKOnly, MAXB>(p, rp, u, h, nb, items, s_ml, s_st, s_bits, lane);
+  if (k == 0) finish_output<D, kKOnly>(p, u, items, s_acc, s_ml, s_w, lane);
+  if (k == 1) finish_row<kKOnly, MAXB>(p, rp, u, h, nb, items, s_ml, s_st, s_bits, lane);
 }
 
 // ---------------------------------------------------------------------------

@@ -180,15 +180,29 @@ def test_maximum_context(torch, dtype, d):
 
 
 @pytest.mark.parametrize("heads,ctxs", [(1, (200, 1000)), (20, (300, 1024)), (20, (700, 3000)),
-                                        (256, (64, 128))])
+                                        (255, (300, 2100)), (256, (64, 128))])
 def test_head_counts(torch, heads, ctxs):
-    """One head; 20 heads (a fused row of more than 16 heads at 1K, rows of
-    several finish workgroups at 3K); 256 heads (beyond the fused kernel's
-    8-bit arrival count, so the two-kernel path)."""
+    """One head; 20 heads (a fused row of more than 16 heads at 1K and at
+    3K); 255 heads (the most the fused kernel's 8-bit arrival count holds,
+    long units); 256 heads (beyond it, so the two-kernel path)."""
     w = synth.Workload(name=f"heads{heads}_{max(ctxs)}", rows=len(ctxs), heads=heads, head_dim=64,
                        dtype="bf16", page_size=16, shuffle=True, alpha=6.0, seed=81, ctx_list=ctxs, hot=2,
                        schedule=(1, 2, 3), eta=0.9)
     run_schedule(w)
+
+
+@pytest.mark.parametrize("max_ctx", [8192, 8224])
+def test_fused_regime_boundary(torch, max_ctx):
+    """The longest context the one-launch kernel takes (8192 tokens, 256
+    blocks) and the first it does not (257 blocks: the static and listed
+    grids with the finish kernel): rows of 8000 and 4500 tokens beside one
+    of max_ctx, through discover, union and sparse depths, each against the
+    oracle."""
+    w = synth.Workload(name=f"boundary{max_ctx}", rows=3, heads=4, head_dim=128, dtype="bf16", page_size=16,
+                       shuffle=True, alpha=5.0, seed=101, ctx_list=(max_ctx, 8000, 4500), hot=6,
+                       schedule=(W.WISE_DISCOVER, W.WISE_DISCOVER_UNION, W.WISE_SPARSE))
+    reps, _ = run_schedule(w)
+    assert all(r.counters[W.CTR_FALLBACKS] == 0 and r.counters[W.CTR_ERRORS] == 0 for r in reps)
 
 
 @pytest.mark.parametrize("rows,heads,tiles,dtype,d", [(8, 16, 16, "bf16", 128), (16, 16, 32, "bf16", 128),
