@@ -56,6 +56,10 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- bytes
 
+def dtype_code(w):
+    return W.WISE_BF16 if w.dtype == "bf16" else W.WISE_F32
+
+
 def attended_blocks(n, mode, support_words_rh):
     """Blocks one (row, head) attends in a call of effective mode ``mode``."""
     nb = (n + 31) // 32
@@ -220,12 +224,13 @@ class ReadProbe:
         self.L.wise_read_probe.restype = ctypes.c_int
 
     @staticmethod
-    def items_for(w, ctx, eff_modes, support_words, fused_units, k_only=False):
+    def items_for(w, ctx, eff_modes, support_words, waves, k_only=False):
         """(items [n, 4] int32, tiles int32, K/V bytes) of one call: every
         (row, head)'s attended blocks cut into items as the library cuts
-        them -- a unit's tiles spread over four waves when the call finishes
-        inside the split kernel, else the call-wide rule (32 tiles when the
-        launch keeps >= 4096 such items, else 16 on that condition, else 8)."""
+        them -- a unit's tiles spread evenly over `waves` waves when the call
+        runs one workgroup per unit (wise_fused_waves() > 0), else the
+        call-wide rule (32 tiles when the launch keeps >= 4096 such items,
+        else 16 on that condition, else 8)."""
         e = 2 if w.dtype == "bf16" else 4
         lists = []
         for r in range(w.rows):
@@ -243,7 +248,7 @@ class ReadProbe:
             n = int(ctx[r])
             toks = np.minimum(32, n - 32 * blocks)
             nbytes += int((1 if k_only else 2) * toks.sum() * w.head_dim * e)
-            t = max(1, -(-c // 4)) if fused_units else T
+            t = max(1, -(-c // waves)) if waves > 0 else T
             assert t <= 64 and (len(blocks) == 0 or (blocks.min() >= 0 and 32 * blocks.max() < n))
             for i in range(0, c, t):
                 items.append((r, h, len(tiles) + i, min(t, c - i)))
@@ -496,9 +501,9 @@ def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=No
     # ---- read ceiling: a pure gather of the same K/V pages in items of the same length ----
     if probe is not None and reuse and dense_reference:
         e = 2 if w.dtype == "bf16" else 4
-        fused = (w.max_ctx + 31) // 32 <= 32
         ceil = {}
         for name, key_kind in ((reuse, reuse), ("dense_same_kv", None)):
+            waves = W.wise_fused_waves(w.rows, w.heads, w.head_dim, w.max_ctx, dtype_code(w), key_kind is not None)
             launches, nbytes, keep = [], [], []
             for rep in range(plan.replicas):
                 if key_kind is None:
@@ -509,7 +514,7 @@ def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=No
                             for pc, key in plan.calls[rep] if key[0] == key_kind
                             for pc_key_kv in [plan.kv[(rep, key[1], key[2] % plan.kv_layers)]]]
                 for kv, eff, sw in lays:
-                    items, tiles, nb = ReadProbe.items_for(w, plan.ctx, eff, sw, fused)
+                    items, tiles, nb = ReadProbe.items_for(w, plan.ctx, eff, sw, waves)
                     it_d = torch.from_numpy(items).to(dev)
                     ti_d = torch.from_numpy(tiles).to(dev)
                     sink = torch.empty(len(items), dtype=torch.int32, device=dev)
@@ -538,12 +543,30 @@ def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=No
         density = set_bits / float(nb.sum() * w.heads)
     else:
         density = float(ctr[W.CTR_SELECTED] / max(1, ctr[W.CTR_CAUSAL]))
+    # the same step with every call dense (no support state), replayed from HIP
+    # graphs: the step-level comparison of WISE decode with dense decode
+    dense_step_ms = None
+    if graphs and not plan.mixed and dense_reference:
+        dgraphs = []
+        for rep in range(plan.replicas):
+            dcalls = [harness.PreparedCall(plan.kv[(rep, depth, layer % plan.kv_layers)], plan.ws, W.WISE_DENSE)
+                      for _, (_, depth, layer) in plan.calls[rep]]
+
+            def run_dense(s, dcalls=dcalls):
+                for dc in dcalls:
+                    dc.run(s)
+            run_dense(sh)
+            dgraphs.append(graph_of(run_dense, torch))
+        dense_step_ms = replay_ms(dgraphs, steps, warmup, torch)
+        del dgraphs
     entry = {"context": CONTEXT_OF.get(w.name, ""), "rows": w.rows,
              "ctx": w.ctx if w.ctx else f"{int(plan.ctx.min())}..{int(plan.ctx.max())}",
              "layers": w.layers, "union_density": round(density, 4),
              "fallbacks_per_step": round(float(ctr[W.CTR_FALLBACKS]) / steps, 2),
              "errors": int(ctr[W.CTR_ERRORS]),
              "ms_per_step": round(step_ms, 4), "rows_per_s": round(w.rows * calls / (step_ms * 1e-3), 1),
+             "dense_ms_per_step": None if dense_step_ms is None else round(dense_step_ms, 4),
+             "wise_step_speedup": None if dense_step_ms is None else round(dense_step_ms / step_ms, 3),
              "calls": out}
     extras = {"plan": plan, "eager_ms": eager_ms, "step_ms": step_ms, "achieved": achieved, "ctr": ctr,
               "calls": calls, "sh": sh}
@@ -557,22 +580,6 @@ def headline_legs(w, plan, dev, sh, steps, warmup, args, out, graphs):
     route, the head-union page route and the support snapshot/restore."""
     import torch
     res = {}
-    calls_per_rep = plan.calls
-    if graphs and not plan.mixed:
-        dgraphs = []
-        for rep in range(plan.replicas):
-            dcalls = [harness.PreparedCall(plan.kv[(rep, depth, layer % plan.kv_layers)], plan.ws, W.WISE_DENSE)
-                      for _, (_, depth, layer) in calls_per_rep[rep]]
-
-            def run(s, dcalls=dcalls):
-                for dc in dcalls:
-                    dc.run(s)
-            run(sh)
-            dgraphs.append(graph_of(run, torch))
-        dense_step_ms = replay_ms(dgraphs, steps, warmup, torch)
-        del dgraphs
-        res["dense_step"] = {"ms_per_step": round(dense_step_ms, 4),
-                             "note": "every call of the step dense, HIP graph replay"}
     st0 = plan.states[0]
     if not args.no_lse_route and not plan.mixed:
         sets = [(layer_dev.attn(), external_lse(layer_dev, plan.ctx, w.page_size)) for layer_dev in plan.kv.values()]
@@ -595,10 +602,10 @@ def headline_legs(w, plan, dev, sh, steps, warmup, args, out, graphs):
             # a pure gather of the same K pages in items of the same length (K only)
             probe = ReadProbe()
             e = 2 if w.dtype == "bf16" else 4
-            fused = (w.max_ctx + 31) // 32 <= 32
+            waves = W.wise_fused_waves(w.rows, w.heads, w.head_dim, w.max_ctx, dtype_code(w), True)
             launches, keep, kb = [], [], 0
             for layer_dev in plan.kv.values():
-                items, tiles, kb = ReadProbe.items_for(w, plan.ctx, np.full(w.rows, W.WISE_DENSE), None, fused,
+                items, tiles, kb = ReadProbe.items_for(w, plan.ctx, np.full(w.rows, W.WISE_DENSE), None, waves,
                                                        k_only=True)
                 it_d, ti_d = torch.from_numpy(items).to(dev), torch.from_numpy(tiles).to(dev)
                 sink = torch.empty(len(items), dtype=torch.int32, device=dev)
@@ -773,11 +780,13 @@ def main():
     rows_per_step = w.rows * ex["calls"]
     achieved = ex["achieved"]   # every timed split launch's algorithmic bytes / its stamped duration
     modes_out = dict(head["calls"])
-    for k in ("dense_step", "lse_discover", "page_union", "offload_state"):
+    if head["dense_ms_per_step"] is not None:
+        modes_out["dense_step"] = {"ms_per_step": head["dense_ms_per_step"],
+                                   "wise_step_speedup": head["wise_step_speedup"],
+                                   "note": "every call of the step dense, HIP graph replay"}
+    for k in ("lse_discover", "page_union", "offload_state"):
         if k in ex:
             modes_out[k] = ex[k]
-    if "dense_step" in modes_out:
-        modes_out["dense_step"]["wise_step_speedup"] = round(modes_out["dense_step"]["ms_per_step"] / ex["step_ms"], 3)
     ctr = ex["ctr"]
     config = {"workload": w.name, "rows": w.rows, "heads": w.heads, "head_dim": w.head_dim,
               "ctx": head["ctx"], "page_size": w.page_size, "layers": w.layers,

@@ -329,6 +329,13 @@ size_t wise_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_
   return make_layout(rows, heads, head_dim, max_ctx, &L) ? L.total : 0;
 }
 
+int32_t wise_fused_waves(int32_t rows, int32_t heads, int32_t head_dim, int32_t max_ctx, int32_t dtype,
+                         int32_t stateful) {
+  Layout L;
+  if ((dtype != WISE_BF16 && dtype != WISE_F32) || !make_layout(rows, heads, head_dim, max_ctx, &L)) return -1;
+  return fused_waves(L, heads, dtype, stateful != 0);
+}
+
 wise_status wise_decode_dense(const wise_attn *a, void *ws, size_t ws_bytes, void *stream) {
   return decode(a, nullptr, WISE_DENSE, nullptr, ws, ws_bytes, stream);
 }

@@ -158,6 +158,47 @@ def traffic(fetch_csv: str, write_csv: str, out_md: str, workload: str, mib: int
     open(out_md, "w").write("\n".join(lines))
 
 
+def parity_classes(record_json, out_md, command):
+    """profiles/ summary of the selection ambiguity classes that one GPU test
+    session recorded (tests/conftest.py writes the JSON when
+    WISE_PARITY_RECORD is set), grouped by workload."""
+    rec = json.load(open(record_json))
+    tot, groups = rec["totals"], {}
+    for r in rec["calls"]:
+        key = r["what"].split(" ")[0]
+        if r["kind"] == "lse":
+            key = "LSE route: " + key
+        g = groups.setdefault(key, {"calls": 0, "units": 0, "near_eta": 0, "near_tie": 0, "mismatch": 0,
+                                    "max_abs": 0.0})
+        g["calls"] += 1
+        for k in ("units", "near_eta", "near_tie", "mismatch"):
+            g[k] += r[k]
+        if r.get("max_abs") is not None:
+            g["max_abs"] = max(g["max_abs"], r["max_abs"])
+    lines = ["# Selection ambiguity classes: GPU vs the fp64 oracle", "",
+             "Every GPU-vs-oracle comparison of one run of the GPU test suite (MI355X),",
+             "grouped by workload.  A unit is one (row, head) of a call; `units` counts",
+             "every unit compared (all modes).  Class A: a discovery unit whose oracle",
+             "running sum lies within 1e-6 of eta at the cut.  Class B: a discovery unit",
+             "(not in class A) whose K-th and (K+1)-th masses tie within 1e-6 relative",
+             "(the exact-tie tests put every unit here on purpose).  A support mismatch",
+             "would be excused only when it is exactly the moved cut (A) or the swapped",
+             "tied pair (B); any other difference fails the test.  The LSE route's rows",
+             "compare supports, tags and counters only (it writes no output).", "",
+             "Command (from the repository root), then this summary:", "", "```", command,
+             "python -m block_sparse_paged_split_amd.profile_summary parity-classes "
+             "gpurun_out/parity_classes.json profiles/parity_classes.md --command '...'", "```", "",
+             f"Totals: {len(rec['calls'])} calls, {tot['units']} units; class A {tot['near_eta']}, "
+             f"class B {tot['near_tie']};",
+             f"support mismatches {tot['mismatch']} (moved cut {tot['excused_a']}, tied swap {tot['excused_b']}).",
+             "", "| workload | calls | units | class A | class B | mismatches | max abs error |",
+             "|---|---|---|---|---|---|---|"]
+    for key, g in groups.items():
+        lines.append(f"| {key} | {g['calls']} | {g['units']} | {g['near_eta']} | {g['near_tie']} | "
+                     f"{g['mismatch']} | {g['max_abs']:.2e} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -173,8 +214,14 @@ def main():
     b.add_argument("--calibrate-mib", type=int, required=True)
     b.add_argument("--algorithmic-bytes", type=float, required=True)
     b.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("parity-classes")
+    c.add_argument("record_json")
+    c.add_argument("out_md")
+    c.add_argument("--command", required=True)
     args = ap.parse_args()
-    if args.what == "kernel-stats":
+    if args.what == "parity-classes":
+        parity_classes(args.record_json, args.out_md, args.command)
+    elif args.what == "kernel-stats":
         kernel_stats(args.stats_csv, args.out_md, args.command)
     else:
         traffic(args.fetch_csv, args.write_csv, args.out_md, args.workload, args.calibrate_mib,

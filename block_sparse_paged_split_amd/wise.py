@@ -27,7 +27,7 @@ BLOCK = 32
 EXPORTED = ("wise_workspace_size", "wise_decode_dense", "wise_decode_discover",
             "wise_decode_sparse", "wise_finish_select", "wise_discover_lse", "wise_compact_pages",
             "wise_snapshot_bytes", "wise_support_snapshot", "wise_support_restore", "wise_status_string",
-            "wise_decode_sparse_noalloc")
+            "wise_decode_sparse_noalloc", "wise_fused_waves")
 SCRATCH_BYTES = 32 << 20  # WISE_SCRATCH_BYTES
 
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.wise_workspace_size.restype = ctypes.c_size_t
         L.wise_workspace_size.argtypes = [ctypes.c_int32] * 4
+        L.wise_fused_waves.restype = ctypes.c_int32
+        L.wise_fused_waves.argtypes = [ctypes.c_int32] * 6
         P, S, V = ctypes.POINTER(WiseAttn), ctypes.POINTER(WiseSupport), ctypes.c_void_p
         L.wise_decode_dense.argtypes = [P, V, ctypes.c_size_t, V]
         L.wise_decode_discover.argtypes = [P, S, ctypes.c_int32, V, ctypes.c_size_t, V]
@@ -116,6 +118,10 @@ def _ref(x):
 
 def wise_workspace_size(rows: int, heads: int, head_dim: int, max_ctx: int) -> int:
     return int(lib().wise_workspace_size(rows, heads, head_dim, max_ctx))
+
+
+def wise_fused_waves(rows: int, heads: int, head_dim: int, max_ctx: int, dtype: int, stateful: bool) -> int:
+    return int(lib().wise_fused_waves(rows, heads, head_dim, max_ctx, dtype, 1 if stateful else 0))
 
 
 def wise_decode_dense(a: WiseAttn, ws: int, ws_bytes: int, stream: int = 0) -> None:

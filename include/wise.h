@@ -169,6 +169,19 @@ typedef struct wise_support {
  * and a finish step over them). */
 size_t wise_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t max_ctx);
 
+/* How a call of these sizes is launched ("What changes", first bullet: the
+ * split kernel and the finish step over its partials).  Returns the waves per
+ * workgroup of the one-launch kernel, which gives each (row, head) one
+ * workgroup whose waves split the unit's attended tiles evenly and then run
+ * the merge, the selection and the bookkeeping themselves (wise_finish_select
+ * then only validates); 0 when the call runs the split grid followed by the
+ * finish kernel; -1 for sizes or a dtype the library does not support.
+ * stateful != 0 for calls given a support state (every call except a
+ * wise_decode_dense without one).  A host-side query: it enqueues nothing
+ * and touches no device. */
+int32_t wise_fused_waves(int32_t rows, int32_t heads, int32_t head_dim, int32_t max_ctx, int32_t dtype,
+                         int32_t stateful);
+
 /* Every row DENSE ("What changes", first bullet: the dense row mode of the
  * split-KV paged decode).  No support state is read or written.  Follow
  * with wise_finish_select(a, NULL, ...). */
@@ -202,11 +215,12 @@ wise_status wise_decode_sparse(const wise_attn *a, const wise_support *s,
  * selected and causal block counts).  `a` and `s` must describe the same call as the decode
  * call (s == NULL after wise_decode_dense).  When the decode call gives each
  * (row, head) one workgroup, it has already done all of this in the same
- * kernel, and this call only validates its arguments: with heads <= 255,
- * every call with max_ctx <= 8192, except plain dense calls (s == NULL) of
- * fewer than 512 (row, head) pairs with max_ctx > 1024 (or > 2048 for small
- * launches of short rows).  It is still required: which shapes finish
- * inside the decode kernel is the library's choice and may change. */
+ * kernel, and this call only validates its arguments (wise_fused_waves()
+ * > 0): with heads <= 255, every call with max_ctx <= 8192, except plain
+ * dense calls (s == NULL) of fewer than 512 (row, head) pairs with max_ctx >
+ * 1024 (or > 2048 for small launches of short rows).  It is still required:
+ * which shapes finish inside the decode kernel is the library's choice and
+ * may change. */
 wise_status wise_finish_select(const wise_attn *a, const wise_support *s, void *ws,
                                size_t ws_bytes, void *stream);
 

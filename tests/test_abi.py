@@ -59,6 +59,28 @@ def test_workspace_size(lib):
         assert W.wise_workspace_size(*bad) == 0
 
 
+def test_fused_waves_regimes(lib):
+    """The host-side launch query: one-launch workgroups of 4-16 waves up to
+    8K tokens and 255 heads, the split grid + finish kernel beyond, and -1
+    for sizes or dtypes the library rejects."""
+    fw = W.wise_fused_waves
+    bf, f32 = W.WISE_BF16, W.WISE_F32
+    assert fw(32, 16, 128, 1024, bf, True) == 4        # four 8-tile items per 1K unit
+    assert fw(32, 16, 128, 1024, bf, False) == 4
+    assert fw(2, 16, 128, 1024, bf, True) in (8, 16)   # small launch: shorter items, more waves
+    assert fw(64, 16, 128, 4096, bf, True) == 8        # >= 512 units: 8 waves
+    assert fw(20, 16, 128, 4096, bf, True) == 16       # fewer units: 16 waves
+    assert fw(20, 16, 128, 4096, f32, True) == 8       # fp32 d128 waves need more registers
+    assert fw(20, 16, 128, 4096, bf, False) == 0       # small plain dense call: split grid
+    assert fw(64, 16, 128, 8192, bf, True) == 8
+    assert fw(64, 16, 128, 8224, bf, True) == 0        # 257 blocks: beyond the one-launch kernel
+    assert fw(4, 256, 128, 1024, bf, True) == 0        # row arrivals are counted in 8 bits
+    assert fw(4, 255, 128, 1024, bf, True) == 4
+    for bad in [(32, 16, 96, 1024, bf, True), (32, 16, 128, 1024, 7, True), (0, 16, 128, 1024, bf, True),
+                (32, 16, 128, 65537, bf, True)]:
+        assert fw(*bad) == -1
+
+
 FAKE = 0x10000  # never dereferenced: every call below fails host validation
 
 
