@@ -141,8 +141,9 @@ def stream_handle() -> int:
 
 def call(layer: DeviceLayer, ws: Workspace, mode: int, state: Optional[SupportState] = None,
          layer_idx: int = 0, required: int = 2, eta: float = 0.95, row_mode=None,
-         events=None, stream: Optional[int] = None) -> None:
-    """One (depth, layer) call: decode (split-KV kernel) + finish."""
+         events=None, stream: Optional[int] = None, finish: bool = True) -> None:
+    """One (depth, layer) call: decode (split-KV kernel) + finish (left out
+    with finish=False, for the tests of what the decode call alone does)."""
     st = stream_handle() if stream is None else stream
     a = layer.attn(events)
     s = state.view(layer_idx, required, eta) if state is not None else None
@@ -154,7 +155,8 @@ def call(layer: DeviceLayer, ws: Workspace, mode: int, state: Optional[SupportSt
         W.wise_decode_discover(a, s, mode == W.WISE_DISCOVER_UNION, ws.ptr, ws.nbytes, st)
     else:
         W.wise_decode_sparse(a, s, None, ws.ptr, ws.nbytes, st)
-    W.wise_finish_select(a, s, ws.ptr, ws.nbytes, st)
+    if finish:
+        W.wise_finish_select(a, s, ws.ptr, ws.nbytes, st)
 
 
 def call_lse(layer: DeviceLayer, ws: Workspace, lse, union: bool, state: SupportState,

@@ -25,12 +25,13 @@ def torch():
     return t
 
 
-@pytest.mark.parametrize("ctx,rows", [(1024, 16), (4096, 8)])
+@pytest.mark.parametrize("ctx,rows", [(1024, 16), (4096, 8), (16384, 4)])
 def test_schedule_reruns_bitwise(torch, ctx, rows):
     """Discover, union, sparse and a mixed launch, rerun twenty times from the
     same state: outputs, supports, tags and counters identical every time.
-    At 1K every call is the fused split + finish; at 4K the static and the
-    listed splits with the finish kernel (multi-workgroup rows)."""
+    At 1K and 4K every call is the one-launch split + finish (short units of
+    four waves; long units of sixteen); at 16K the static and the listed
+    splits with the finish kernel (rows over several workgroups)."""
     w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=rows, ctx=ctx, name=f"rerun{ctx}")
     devs = [harness.upload(synth.layer_inputs(w, d)) for d in range(4)]
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
@@ -86,3 +87,45 @@ def test_fallback_rows_equal_dense_bitwise(torch, ctx):
     torch.cuda.synchronize()
     assert int(st.counters[W.CTR_FALLBACKS].item()) - fb0 == 3 + w.rows
     assert torch.equal(d2.out, dense)
+
+
+@pytest.mark.parametrize("ctx,rows", [(1024, 8), (4096, 4), (2112, 32)])
+def test_one_launch_decode_completes_the_call(torch, ctx, rows):
+    """For shapes with wise_fused_waves() > 0 the decode call alone writes the
+    outputs, the supports, the tags and the counters; wise_finish_select adds
+    nothing.  A schedule run without any finish call must equal, bit for
+    bit, the same schedule with them (short units of a small launch; long
+    units of sixteen waves; long units of eight waves in a launch of 512
+    units)."""
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=rows, ctx=ctx, name=f"decode_only{ctx}")
+    waves = W.wise_fused_waves(w.rows, w.heads, w.head_dim, w.max_ctx, W.WISE_BF16, True)
+    assert waves > 0
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    modes = torch.tensor(([3, 1, 0, 2] * rows)[:rows], dtype=torch.uint8, device="cuda")
+    hosts = [synth.layer_inputs(w, d) for d in range(4)]
+    runs = []
+    for finish in (True, False):
+        devs = [harness.upload(h) for h in hosts]
+        st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+        st.row_position.fill_(2)
+        harness.call(devs[0], ws, W.WISE_DISCOVER, st, required=2, finish=finish)
+        harness.call(devs[1], ws, W.WISE_DISCOVER_UNION, st, required=2, finish=finish)
+        harness.call(devs[2], ws, W.WISE_SPARSE, st, required=2, finish=finish)
+        harness.call(devs[3], ws, W.WISE_SPARSE, st, required=2, row_mode=modes, finish=finish)
+        torch.cuda.synchronize()
+        runs.append([d.out.clone() for d in devs] + [st.support.clone(), st.tags.clone(), st.counters.clone()])
+        say(f"[decode_only{ctx}] waves {waves} finish={finish} counters {st.counters.cpu().numpy()}")
+        del devs
+    for a, b, what in zip(runs[0], runs[1], ("discover", "union", "sparse", "mixed", "support", "tags",
+                                             "counters")):
+        assert torch.equal(a, b), f"{what} differs without the finish call"
+    assert int(runs[0][6][W.CTR_SELECTED]) > 0 and not torch.isnan(runs[0][0]).any()
+    if W.wise_fused_waves(w.rows, w.heads, w.head_dim, w.max_ctx, W.WISE_BF16, False) > 0:
+        dev = harness.upload(hosts[0])
+        harness.call(dev, ws, W.WISE_DENSE, finish=False)
+        torch.cuda.synchronize()
+        d_only = dev.out.clone()
+        dev.out.fill_(float("nan"))
+        harness.call(dev, ws, W.WISE_DENSE)
+        torch.cuda.synchronize()
+        assert torch.equal(d_only, dev.out), "dense decode alone differs"
