@@ -16,17 +16,19 @@
 //    (row, head)'s tile list); each wave plans its own item (tag check,
 //    fallback, tile count, compacted tile list), so that a call needs no
 //    host readback.  Three launch shapes share the per-item body: the fused
-//    kernel (one workgroup per unit whose waves cover all of its items, then
-//    finish the unit in the same kernel), the static grid (four independent
-//    waves per workgroup over every (unit, item) slot, finished by the
-//    finish kernel), and the listed grid (persistent waves over the compact
-//    item list a one-workgroup plan kernel builds, for calls with sparse
-//    rows whose units span several workgroups).  Items keep about eight
-//    tiles unless the launch is large enough to outlast any one item many
-//    times over; then they grow to 16 or 32 tiles (decided on the host for
-//    calls with no sparse rows, in the plan kernel from the attended tiles
-//    otherwise), since each item's partial (m, l, acc) written to HBM amid
-//    the K/V stream costs far more than its bytes.
+//    kernel (one workgroup per (row, head) unit of up to 256 blocks, i.e.
+//    contexts up to 8K, whose 4-16 waves split the unit's tiles evenly and
+//    then finish the unit in the same kernel), and, for longer contexts,
+//    the static grid (four independent waves per workgroup over every
+//    (unit, item) slot, finished by the finish kernel) and the listed grid
+//    (persistent waves over the compact item list a one-workgroup plan
+//    kernel builds, for calls with sparse rows).  In those two grids items
+//    keep about eight tiles unless the launch is large enough to outlast
+//    any one item many times over; then they grow to 16 or 32 tiles
+//    (decided on the host for calls with no sparse rows, in the plan kernel
+//    from the attended tiles otherwise), since each item's partial
+//    (m, l, acc) written to HBM amid the K/V stream costs far more than its
+//    bytes.
 //  * A 32-token K (or V) tile is read with 16-byte loads in which each load
 //    instruction covers TPI whole tokens contiguously (1 KB per wave for
 //    bf16 d=128): lane = (token subgroup g, 16-byte dim chunk c).  Every K
@@ -509,8 +511,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
 }
 
 // ---------------------------------------------------------------------------
-// Fused split + finish, for calls whose units fit one workgroup each: the
-// items leave their partials and tile stats in LDS, and two waves then finish
+// Fused split + finish, for calls whose units fit one workgroup each (see
+// fused_waves()): the waves leave their partials and tile stats in LDS, and
+// two waves then finish
 // the unit side by side.  Wave 0 merges the partials into the output exactly
 // as the finish kernel would (the same merge in the same order, so the
 // output bits do not depend on which kernel ran it); wave 1 runs the eta
