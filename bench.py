@@ -135,6 +135,9 @@ def _oracle_worker(w, rows, min_s):
     R = w.rows
     inputs = [synth.layer_inputs(w, depth, 0, rows=rows, workers=1) for depth in range(len(w.schedule))]
     done, t_total, passes = 0, 0.0, 0
+    classes = {"discovery_units": 0, "class_a": 0, "class_b": 0}
+    union = None
+    discover_modes = (O.DISCOVER, O.DISCOVER_UNION)
     with threadpool_limits(1):
         while passes < 1 or t_total < min_s:   # pass 0 (first touch of the inputs) is not timed
             passes += 1
@@ -152,8 +155,37 @@ def _oracle_worker(w, rows, min_s):
                 if passes > 1:
                     t_total += time.perf_counter() - t0
                     done += len(rows)
+                elif mode in discover_modes:
+                    # the selection's ambiguity classes, from the untimed pass
+                    for u in res.units.values():
+                        if u.selection is None:
+                            continue
+                        a = u.selection.near_eta(w.eta)
+                        classes["discovery_units"] += 1
+                        classes["class_a"] += int(a)
+                        classes["class_b"] += int(not a and u.selection.near_tie())
+                    union = res.support[rows].copy()
                 sup, tags = res.support, res.tags
-    return done, t_total
+    return done, t_total, classes, union
+
+
+def device_copy_gbs(dev, mib=1024, reps=10):
+    """Bytes read + written per second by a plain device-to-device copy of
+    ``mib`` MiB (torch's copy_), the mean over ``reps`` copies."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
 def host_facts():
@@ -179,11 +211,33 @@ def cpu_baseline(w, pool, workers, facts, min_s=1.5):
     wall = max(r[1] for r in res)
     cpu = sum(r[1] for r in res)
     nproc, model = facts
-    return {"value": round(done / wall, 2), "unit": "rows/s", "cores": len(chunks), "kind": "oracle",
-            "sample": f"all {w.rows} rows of {w.name} x {len(w.schedule)} depths, repeated; {done} row-calls "
-                      f"in {len(chunks)} processes ({cpu:.1f} s of oracle CPU time, slowest {wall:.2f} s); "
-                      f"fp64 numpy, 1 BLAS thread per process",
-            "nproc": nproc, "cpu_model": model, "blas_threads_per_process": 1}
+    classes = {k: sum(r[2][k] for r in res) for k in res[0][2]}
+    union = None
+    if all(r[3] is not None for r in res):
+        union = np.concatenate([r[3] for r in res])   # rows in order: the chunks are consecutive
+    baseline = {"value": round(done / wall, 2), "unit": "rows/s", "cores": len(chunks), "kind": "oracle",
+                "sample": f"all {w.rows} rows of {w.name} x {len(w.schedule)} depths, repeated; {done} row-calls "
+                          f"in {len(chunks)} processes ({cpu:.1f} s of oracle CPU time, slowest {wall:.2f} s); "
+                          f"fp64 numpy, 1 BLAS thread per process",
+                "nproc": nproc, "cpu_model": model, "blas_threads_per_process": 1}
+    return baseline, classes, union
+
+
+def selection_parity(classes, union_oracle, support_gpu, w):
+    """The headline step's selection beside the oracle's: ambiguity classes
+    of every discovery unit (class A: the oracle's cut within 1e-6 of eta;
+    class B: its K-th and (K+1)-th masses tied within 1e-6), and the (row,
+    head) units whose union support after the step differs from the
+    oracle's, counted before any exemption."""
+    out = dict(classes)
+    if union_oracle is not None:
+        gpu = support_gpu[:w.rows, 0]                    # [rows, heads, words] of replica 0
+        orc = union_oracle[:, 0]
+        out["union_units"] = int(w.rows * w.heads)
+        out["union_mismatches"] = int((gpu != orc).any(axis=-1).sum())
+    out["what"] = (f"fp64 oracle on the {w.name} step's inputs (replica 0) beside the GPU's union support "
+                   f"after the timed steps")
+    return out
 
 
 # ----------------------------------------------------------------------------- counters
@@ -569,15 +623,15 @@ def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=No
              "wise_step_speedup": None if dense_step_ms is None else round(dense_step_ms / step_ms, 3),
              "calls": out}
     extras = {"plan": plan, "eager_ms": eager_ms, "step_ms": step_ms, "achieved": achieved, "ctr": ctr,
-              "calls": calls, "sh": sh}
+              "calls": calls, "sh": sh, "support_r0": sup_of[0]}
     if headline:
         extras.update(headline_legs(w, plan, dev, sh, steps, warmup, args, out, graphs))
     return entry, extras
 
 
 def headline_legs(w, plan, dev, sh, steps, warmup, args, out, graphs):
-    """The legs only the headline line reports: the all-dense step, the LSE
-    route, the head-union page route and the support snapshot/restore."""
+    """The legs only the headline line reports: the LSE route, the
+    head-union page route and the support snapshot/restore."""
     import torch
     res = {}
     st0 = plan.states[0]
@@ -796,6 +850,7 @@ def main():
               "timing": "eager launches" if args.no_graph else "HIP graph replay of whole steps",
               "union_density": head["union_density"], "fallbacks_per_step": head["fallbacks_per_step"],
               "errors": head["errors"]}
+    support_r0 = ex["support_r0"]
     plan.free()
     del ex, plan
     torch.cuda.empty_cache()
@@ -830,14 +885,19 @@ def main():
         "roofline": None,
         "cpu_baseline": None,
     }
-    # roofline of the dominant kernel: the split kernel of the headline's calls
+    # roofline of the dominant kernel: the split kernel of the headline's calls;
+    # beside the published peak, the box's own device-to-device copy rate
+    copy_gbs = device_copy_gbs(dev)
     out["roofline"] = {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 1),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                       "traffic": measured_traffic(w.name)}
+                       "traffic": measured_traffic(w.name),
+                       "device_copy": round(copy_gbs, 1), "frac_of_device_copy": round(achieved / copy_gbs, 4)}
     if pool is not None:
         log("cpu baseline: the oracle on the headline rows, in worker processes")
-        out["cpu_baseline"] = cpu_baseline(w, pool, workers, facts)
+        out["cpu_baseline"], classes, union = cpu_baseline(w, pool, workers, facts)
         pool.shutdown()
+        if w.mix is None and w.fixed_density is None:
+            out["selection_parity"] = selection_parity(classes, union, support_r0, w)
     print(json.dumps(out), flush=True)
 
 
