@@ -664,6 +664,35 @@ __device__ __forceinline__ void finish_row(const SplitParams &p, const RowPlan &
 
 // MAXB: the most blocks a unit of the launch has (64, or 256 for contexts up
 // to 8K); a wave's share of a unit is at most ceil(MAXB / W) list entries.
+// The unit a fused workgroup takes.  A launch of per-row modes over at most
+// 64 rows takes its rows heaviest first: rows that attend in full (dense,
+// discovery) before sparse rows, then longer contexts first, then by index.
+// The longest units then start in the first round of workgroups instead of
+// queueing behind short ones that happened to come first (the order of a
+// longest-processing-time-first schedule).  Other launches take the units in
+// index order.  Every workgroup computes the same permutation from the same
+// keys (unique, since the row index is part of each), so every unit is taken
+// exactly once; the heads of a row stay on consecutive workgroups, spread
+// over the XCDs.
+__device__ __forceinline__ void fused_unit(const SplitParams &p, int lane, int &r, int &h) {
+  const int b = blockIdx.x;
+  const int pos = b / p.heads;
+  h = b - pos * p.heads;
+  r = pos;
+  if (p.row_mode == nullptr || p.rows > 64) return;
+  uint32_t key = 0xFFFFFFFFu;
+  if (lane < p.rows) {
+    const int n = min(max(p.ctx_len[lane], 0), kMaxCtx);
+    key = (p.row_mode[lane] == WISE_SPARSE ? 1u << 23 : 0u) | (static_cast<uint32_t>(kMaxCtx - n) << 6) |
+          static_cast<uint32_t>(lane);
+  }
+  int rank = 0;
+  for (int j = 0; j < p.rows; ++j)
+    rank += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), j)) < key ? 1 : 0;
+  const unsigned long long hit = __ballot(lane < p.rows && rank == pos);
+  r = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(hit)) - 1);
+}
+
 template <bool kBf16, int D, int W, bool kKOnly, int MAXB>
 __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p) {
   constexpr int kTiles = (MAXB + W - 1) / W > kMaxTilesPerItem ? (MAXB + W - 1) / W : kMaxTilesPerItem;
@@ -677,9 +706,9 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   __shared__ uint32_t s_bits[MAXB / 32];
   const int lane = threadIdx.x & 63;
   const int k = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);  // item slot
-  const int u = blockIdx.x;  // unit = (row, head); units of a row spread over the XCDs
-  const int r = u / p.heads;
-  const int h = u - r * p.heads;
+  int r, h;
+  fused_unit(p, lane, r, h);
+  const int u = r * p.heads + h;  // unit = (row, head)
   const RowPlan rp = plan_row(p, r, h, lane);
   const int nb = rp.bad ? 0 : (rp.n + kBlock - 1) / kBlock;
   const bool sparse = !rp.bad && rp.eff == WISE_SPARSE;
