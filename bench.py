@@ -832,6 +832,16 @@ def main():
                        probe=probe, headline=True, args=args, dense_reference=not args.no_dense_reference)
     plan = ex["plan"]
     rows_per_step = w.rows * ex["calls"]
+    # the read ceiling of the step's split launches: the pure gather of the
+    # same pages (reuse calls: their own supports; discovery calls: the dense
+    # pages), weighted by how often each kind runs in a step
+    step_ceiling = None
+    ceil = head["calls"].get("read_ceiling")
+    if ceil:
+        kinds = [key[0] for _, key in plan.calls[0]]
+        pick = [ceil[k] if k in ceil else ceil.get("dense_same_kv") for k in kinds]
+        if all(c is not None for c in pick):
+            step_ceiling = sum(c["kv_MB"] for c in pick) * 1e6 / (sum(c["us"] for c in pick) * 1e-6) / 1e9
     achieved = ex["achieved"]   # every timed split launch's algorithmic bytes / its stamped duration
     modes_out = dict(head["calls"])
     if head["dense_ms_per_step"] is not None:
@@ -892,6 +902,9 @@ def main():
                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": measured_traffic(w.name),
                        "device_copy": round(copy_gbs, 1), "frac_of_device_copy": round(achieved / copy_gbs, 4)}
+    if step_ceiling:
+        out["roofline"].update({"read_ceiling": round(step_ceiling, 1),
+                                "frac_of_read_ceiling": round(achieved / step_ceiling, 4)})
     if pool is not None:
         log("cpu baseline: the oracle on the headline rows, in worker processes")
         out["cpu_baseline"], classes, union = cpu_baseline(w, pool, workers, facts)
