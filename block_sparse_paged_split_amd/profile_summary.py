@@ -187,7 +187,7 @@ def parity_classes(record_json, out_md, command):
              "compare supports, tags and counters only (it writes no output).", "",
              "Command (from the repository root), then this summary:", "", "```", command,
              "python -m block_sparse_paged_split_amd.profile_summary parity-classes "
-             "gpurun_out/parity_classes.json profiles/parity_classes.md --command '...'", "```", "",
+             "$OUT/parity_classes.json profiles/parity_classes.md --command '...'", "```", "",
              f"Totals: {len(rec['calls'])} calls, {tot['units']} units; class A {tot['near_eta']}, "
              f"class B {tot['near_tie']};",
              f"support mismatches {tot['mismatch']} (moved cut {tot['excused_a']}, tied swap {tot['excused_b']}).",
