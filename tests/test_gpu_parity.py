@@ -306,14 +306,14 @@ def test_plan_many_units(torch):
 
 
 def test_page_size_and_layout_invariance(torch):
-    """Physical layout changes nothing: same bits for page sizes 8..512 (at
-    512 every row sits in one page), a shuffled or identity block table, and
-    [pages, P, H, d] storage."""
+    """Physical layout changes nothing: same bits for page sizes 8..4096 (from
+    512 on every row sits in one page; 4096 is the largest supported), a
+    shuffled or identity block table, and [pages, P, H, d] storage."""
     base = synth.Workload(name="layout", rows=6, heads=4, head_dim=128, dtype="bf16", page_size=8,
                           shuffle=True, alpha=4.0, seed=5, ctx_list=(5, 40, 64, 129, 300, 511),
                           hot=2, schedule=(1,))
     outs = []
-    for P in (8, 16, 32, 64, 128, 512):
+    for P in (8, 16, 32, 64, 128, 512, 4096):
         for shuffle in (True, False):
             w = dataclasses.replace(base, page_size=P, shuffle=shuffle)
             say(f"[layout] P={P} shuffle={shuffle}")
