@@ -188,6 +188,68 @@ def device_copy_gbs(dev, mib=1024, reps=10):
     return 2 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
+def _oracle_modes_worker(w, rows):
+    """The fp64 oracle on ``rows`` of workload ``w`` (its first KV set, layer
+    0), one call per mode: dense and discover on depth 0, union on depth 1
+    (after that discovery), sparse on depth 2 (over the union, or over the
+    support set directly for a fixed-density workload).  Returns {mode:
+    (row-calls, seconds)}; inputs are generated first and not timed."""
+    from threadpoolctl import threadpool_limits
+    from oracle import wise_oracle as O
+    R = w.rows
+    ctx = synth.context_lengths(w)
+    words = (w.max_ctx + 1023) // 1024
+    depths = [synth.layer_inputs(w, d, 0, rows=rows, workers=1) for d in range(3)]
+    req, pos = np.arange(R) + 1000, np.zeros(R, np.int64)
+    out = {}
+
+    def call(li, mode, sup, tags, reps=3):
+        ts = []
+        for _ in range(reps):   # the median of a few calls from the same state
+            t0 = time.perf_counter()
+            res = O.run_call(q=li.q, k_cache=li.k, v_cache=li.v, block_table=li.block_table,
+                             ctx_len=li.ctx_len, page_size=w.page_size, num_pages=li.num_pages,
+                             max_ctx=w.max_ctx, modes=[mode] * R, support=sup, tags=tags, row_request=req,
+                             row_position=pos, required=1, eta=w.eta, rows=rows)
+            ts.append(time.perf_counter() - t0)
+        return res, float(np.median(ts))
+
+    with threadpool_limits(1):
+        empty = lambda: (np.zeros((R, 1, w.heads, words), np.uint32), np.zeros((R, 1), O.TAG_DTYPE))
+        call(depths[0], O.DENSE, *empty(), reps=1)               # first touch, not timed
+        _, t = call(depths[0], O.DENSE, *empty())
+        out["dense"] = (len(rows), t)
+        if w.fixed_density is not None:
+            sup, tags = empty()
+            sup[:, 0] = synth.random_support(w, w.fixed_density, ctx, words)
+            tags["request"][:, 0], tags["position"][:, 0], tags["discoveries"][:, 0] = req, pos, 1
+        else:
+            res, t = call(depths[0], O.DISCOVER, *empty())
+            out["discover"] = (len(rows), t)
+            res, t = call(depths[1], O.DISCOVER_UNION, res.support, res.tags)
+            out["discover_union"] = (len(rows), t)
+            sup, tags = res.support, res.tags
+        _, t = call(depths[2], O.SPARSE, sup, tags)
+        out["sparse"] = (len(rows), t)
+    return out
+
+
+def cpu_oracle_by_mode(w, pool, workers, max_rows=16):
+    """Oracle rows/s per mode on a bounded sample of a workload: up to
+    ``max_rows`` rows (spread over its context lengths), one row per worker
+    process; rate = row-calls / the slowest worker's seconds for that mode."""
+    R = w.rows
+    pick = np.unique(np.linspace(0, R - 1, min(max_rows, R)).round().astype(int))
+    res = [f.result() for f in [pool.submit(_oracle_modes_worker, w, [int(r)]) for r in pick]]
+    rates = {}
+    for mode in res[0]:
+        calls = sum(r[mode][0] for r in res)
+        slowest = max(r[mode][1] for r in res)
+        rates[mode] = round(calls / slowest, 1)
+    return {"rows_per_s": rates, "cores": min(workers, len(pick)),
+            "sample": f"{len(pick)} rows of {w.name} (one per process), the median of 3 oracle calls per mode"}
+
+
 def host_facts():
     model = "unknown"
     try:
@@ -529,7 +591,8 @@ def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=No
             if name == "dense_same_kv":
                 out[name] = {"algorithmic_MB": round(dense_bytes / 1e6, 3)}
             mb = out[name]["algorithmic_MB"]
-            out[name].update({"call_us": round(call_us, 2), "call_GBps": round(mb * 1e6 / (call_us * 1e-6) / 1e9, 1),
+            out[name].update({"call_us": round(call_us, 2), "call_rows_per_s": round(w.rows / (call_us * 1e-6), 1),
+                              "call_GBps": round(mb * 1e6 / (call_us * 1e-6) / 1e9, 1),
                               "call_frac": round(mb * 1e6 / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     # split-stamped dense reference, rotating over every KV set of the run
     n_it = max(16, 2 * len(dense_pcs)) if dense_reference else 0
@@ -908,6 +971,12 @@ def main():
     if pool is not None:
         log("cpu baseline: the oracle on the headline rows, in worker processes")
         out["cpu_baseline"], classes, union = cpu_baseline(w, pool, workers, facts)
+        for name, entry in contexts.items():
+            wc = synth.WORKLOADS[name]
+            if wc.layers > 1:
+                wc = dataclasses.replace(wc, layers=1)
+            log(f"cpu oracle by mode: {name}")
+            entry["cpu_oracle"] = cpu_oracle_by_mode(wc, pool, workers)
         pool.shutdown()
         if w.mix is None and w.fixed_density is None:
             out["selection_parity"] = selection_parity(classes, union, support_r0, w)
