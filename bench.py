@@ -557,6 +557,7 @@ def measure(w, dev, *, steps, warmup, replicas, kv_layers, graphs=True, probe=No
     for name, m in kinds.items():
         ms, by = np.asarray(m["ms"]), np.asarray(m["bytes"], np.float64)
         out[name] = {"split_us": round(float(ms.mean()) * 1e3, 2),
+                     "split_us_median": round(float(np.median(ms)) * 1e3, 2),
                      "split_us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
                      "split_us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2),
                      "algorithmic_MB": round(float(by.mean()) / 1e6, 3),
