@@ -14,8 +14,19 @@ from HIP graphs.  ``contexts`` holds, for the 1K / 4K / 8K workloads and the
 ragged batch, every call kind's time -- the split kernel alone (stamped with
 its own start and stop) and the whole call (every kernel it launches, timed
 by HIP-graph replay of back-to-back calls) -- its algorithmic bytes, GB/s,
-fraction of the 8 TB/s HBM peak, sparse vs dense on the same KV, and the
-time a pure gather of the same K/V pages in items of the same length takes.
+fraction of the 8 TB/s HBM peak, sparse vs dense on the same KV, the time a
+pure gather of the same K/V pages in items of the same length takes, the
+all-dense step beside the WISE step, and the fp64 oracle's rows/s per mode
+on a bounded sample of the same rows (``cpu_oracle``).
+
+``roofline``: the split kernel of the headline's calls -- algorithmic bytes
+over kernel-stamped durations against the 8 TB/s peak, the HBM bytes the
+committed counter summary recorded for it (while its sources are unchanged),
+the box's device-to-device copy rate and the read ceiling of the same
+launches.  ``cpu_baseline``: the oracle on the headline rows in worker
+processes (the host share of one GPU).  ``selection_parity``: the headline
+step's selection beside the oracle's (ambiguity classes, union supports that
+differ).
 """
 
 from __future__ import annotations
