@@ -20,7 +20,9 @@
  *     wise_finish_select            (same workspace, same stream, next)
  * The decode call runs the split-KV kernel (one launch, every row mode);
  * the finish call merges the splits into `out`, runs the eta selection for
- * discovery rows, updates the bitmask, the tags and the counters.
+ * discovery rows, updates the bitmask, the tags and the counters.  For
+ * contexts up to 8K (wise_fused_waves() > 0) the decode call's one kernel
+ * already does all of that, and the finish call only validates.
  *
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers owned by the caller; they are
