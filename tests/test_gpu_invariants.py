@@ -3,6 +3,7 @@ same bits (a race detector for the in-kernel barriers and atomics), and the
 rows that fall back to dense equal a dense call's rows bit for bit."""
 
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -25,19 +26,24 @@ def torch():
     return t
 
 
-@pytest.mark.parametrize("ctx,rows", [(1024, 16), (4096, 8), (16384, 4)])
+RERUNS = int(os.environ.get("WISE_RERUNS", "20"))
+
+
+@pytest.mark.parametrize("ctx,rows", [(1024, 16), (4096, 8), (4096, 20), (8192, 10), (16384, 4)])
 def test_schedule_reruns_bitwise(torch, ctx, rows):
-    """Discover, union, sparse and a mixed launch, rerun twenty times from the
-    same state: outputs, supports, tags and counters identical every time.
-    At 1K and 4K every call is the one-launch split + finish (short units of
-    four waves; long units of sixteen); at 16K the static and the listed
-    splits with the finish kernel (rows over several workgroups)."""
+    """Discover, union, sparse and a mixed launch, rerun WISE_RERUNS times
+    (20 by default) from the same state: outputs, supports, tags and counters
+    identical every time.  Up to 8K every call is the one-launch split +
+    finish (short units of four waves; long units of sixteen, the mixed
+    launch taking its rows heaviest first; 320 units need a second round of
+    workgroups); at 16K the static and the listed splits with the finish
+    kernel (rows over several workgroups)."""
     w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=rows, ctx=ctx, name=f"rerun{ctx}")
     devs = [harness.upload(synth.layer_inputs(w, d)) for d in range(4)]
     ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
     modes = torch.tensor(([3, 1, 0, 2] * rows)[:rows], dtype=torch.uint8, device="cuda")
     ref = None
-    for it in range(20):
+    for it in range(RERUNS):
         st = harness.SupportState(w.rows, w.heads, w.max_ctx)
         st.row_position.fill_(2)
         harness.call(devs[0], ws, W.WISE_DISCOVER, st, required=2)
