@@ -513,17 +513,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void split_static_kernel(const
 // ---------------------------------------------------------------------------
 // Fused split + finish, for calls whose units fit one workgroup each (see
 // fused_waves()): the waves leave their partials and tile stats in LDS, and
-// two waves then finish
-// the unit side by side.  Wave 0 merges the partials into the output exactly
-// as the finish kernel would (the same merge in the same order, so the
-// output bits do not depend on which kernel ran it); wave 1 runs the eta
-// selection, writes or ORs the support and does the row's bookkeeping.  Both
-// compute the unit's (M, L) by the same operations, so they agree bit for
-// bit.  A discovery row's tag and density counters are updated by the last
-// of its heads to arrive, counted in the tag's reserved word (arrivals |
-// error heads << 8 | newly selected blocks << 16), which that last arrival
-// returns to zero.  Every unit of the row planned from the tag before any
-// head arrives, so the update cannot race with a plan.
+// two waves then finish the unit side by side.  Wave 1 runs the eta
+// selection and writes or ORs the support; wave 0 merges the partials into
+// the output exactly as the finish kernel would (the same merge in the same
+// order, so the output bits do not depend on which kernel ran it).  A
+// discovery row's tag and density counters are updated by the last of its
+// heads to arrive, counted in the tag's reserved word.  For short units of
+// calls that read V, wave 0 sends the arrival (arrivals | error heads << 8)
+// before its output stores and each head's selection wave adds its newly
+// selected blocks to the density counter itself, so the arrival does not
+// wait for the selection.  Otherwise -- long units, and the LSE route, whose
+// short K-only launch would end with a burst of same-address counter
+// atomics -- the selection wave carries the arrival with the row's selected
+// blocks (<< 16 in the same word).
+// Both waves compute the unit's (M, L) by the same operations, so they agree
+// bit for bit.  The last arrival returns the word to zero.  Every unit of
+// the row planned from the tag before any head arrives, so the update
+// cannot race with a plan.
 // ---------------------------------------------------------------------------
 // (M, L) of a unit from its items' partials in LDS: M = max m_i, L = sum
 // l_i 2^(m_i - M) (or M = the external LSE in base-2 units and L = 1 on the
@@ -552,7 +558,7 @@ __device__ __forceinline__ void unit_norm(const SplitParams &p, int u, int items
 }
 
 // Wave 0: the output (NaN for a unit with bad data) and its error count.
-// The LSE route writes no output; wave 1 counts its errors.
+// The LSE route writes no output; its selection wave counts its errors.
 template <int D, bool kKOnly>
 __device__ __forceinline__ void finish_output(const SplitParams &p, int u, int items, const float *s_acc,
                                               const float2 *s_ml, float *s_w, int lane) {
@@ -573,11 +579,65 @@ __device__ __forceinline__ void finish_output(const SplitParams &p, int u, int i
   }
 }
 
+// Short units of calls that read V split the finish the other way (see the
+// fused kernel): wave 0 writes the output and sends the row's arrival before
+// its output stores, so their round trips overlap, and the last head to
+// arrive updates the tag and the causal-block count; wave 1 selects, writes
+// the support and adds its own newly selected blocks to the density counter.
+template <int D>
+__device__ __forceinline__ void finish_output_arrive(const SplitParams &p, const RowPlan &rp, int u, int h, int nb,
+                                                     int items, const float *s_acc, const float2 *s_ml, float *s_w,
+                                                     int lane) {
+  const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
+  const bool discover = stateful && (rp.eff == WISE_DISCOVER || rp.eff == WISE_DISCOVER_UNION);
+  float M, L;
+  bool err;
+  unit_norm<false>(p, u, items, s_ml, s_w, lane, M, L, err);
+  wise_tag *tag = stateful ? p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer : nullptr;
+  unsigned int *arrive = discover ? reinterpret_cast<unsigned int *>(&tag->reserved) : nullptr;
+  unsigned int all = 0u;
+  if (discover && lane == 0) {
+    const unsigned int mine = 1u | (err ? 1u << 8 : 0u);
+    all = atomicAdd(arrive, mine) + mine;
+  }
+  sel::wave_lds_sync();
+  constexpr int kOut = D / 64;  // output elements per lane
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int dd = lane + 64 * i;
+    float a = 0.0f;
+    for (int t = 0; t < items; ++t) a = fmaf(s_acc[t * D + dd], s_w[t], a);
+    p.out[static_cast<int64_t>(u) * D + dd] = err ? __builtin_nanf("") : a / L;
+  }
+  if (err && lane == 0 && p.counters) atomicAdd(p.counters + WISE_CTR_ERRORS, 1ull);
+  if (!stateful || lane != 0) return;
+  if (!discover) {
+    // a union row whose discovery window is broken ran dense: the rest of
+    // this token runs dense too
+    if (rp.req == WISE_DISCOVER_UNION && h == 0) tag->discoveries = 0;
+    return;
+  }
+  if (static_cast<int>(all & 0xFFu) != p.heads) return;
+  atomicExch(arrive, 0u);
+  const int err_heads = static_cast<int>((all >> 8) & 0xFFu);
+  if (p.counters && rp.eff == WISE_DISCOVER)
+    atomicAdd(p.counters + WISE_CTR_CAUSAL, static_cast<unsigned long long>(nb) * (p.heads - err_heads));
+  // a bad page in any head of the row breaks this discovery
+  if (rp.eff == WISE_DISCOVER) {
+    tag->request = p.row_request[rp.row];
+    tag->position = p.row_position[rp.row];
+    tag->discoveries = err_heads ? 0 : 1;
+  } else {
+    tag->discoveries = err_heads ? 0 : tag->discoveries + 1;
+  }
+}
+
 // Wave 1: the eta selection of a discovery unit, the support words written
 // (DISCOVER) or ORed (DISCOVER_UNION; into the words its plan loaded -- no
-// other unit writes them), the row's arrival and, for its last head, the tag
-// and the density counters.
-template <bool kKOnly, int MAXB>
+// other unit writes them) and its newly selected blocks counted; on the LSE
+// route also the row's arrival and, for its last head, the tag and the
+// density counters.
+template <bool kKOnly, int MAXB, bool kArrives>
 __device__ __forceinline__ void finish_row(const SplitParams &p, const RowPlan &rp, int u, int h, int nb, int items,
                                            const float2 *s_ml, const float2 *s_st, uint32_t *s_bits, int lane) {
   const bool stateful = p.support != nullptr && !rp.bad && rp.req != WISE_DENSE;
@@ -585,8 +645,9 @@ __device__ __forceinline__ void finish_row(const SplitParams &p, const RowPlan &
   wise_tag *tag = stateful ? p.tags + static_cast<int64_t>(rp.slot) * p.layers + p.layer : nullptr;
   if (!discover) {
     // a union row whose discovery window is broken ran dense (on the LSE
-    // route it did no work): the rest of this token runs dense too
-    if (stateful && rp.req == WISE_DISCOVER_UNION && h == 0 && lane == 0) tag->discoveries = 0;
+    // route it did no work): the rest of this token runs dense too (done by
+    // the wave that carries the arrival)
+    if (kArrives && stateful && rp.req == WISE_DISCOVER_UNION && h == 0 && lane == 0) tag->discoveries = 0;
     if (!kKOnly || !rp.bad) return;
   }
   float M, L;
@@ -629,6 +690,20 @@ __device__ __forceinline__ void finish_row(const SplitParams &p, const RowPlan &
     }
   }
   const int selected = err ? 0 : rp.eff == WISE_DISCOVER ? K : sel::wave_sum_int(__popc(nw & ~rp.word));
+  if constexpr (!kArrives) {
+    // wave 0 carries the row's arrival; this wave adds its own newly
+    // selected blocks to the density counter
+    if (err) return;
+    uint32_t *sw = p.support + ((static_cast<int64_t>(rp.slot) * p.layers + p.layer) * p.heads + h) * p.words;
+    if (rp.eff == WISE_DISCOVER) {
+      for (int w = lane; w < p.words; w += 64) sw[w] = w == lane ? nw : 0u;
+    } else if (lane < p.words && (nw & ~rp.word) != 0u) {
+      sw[lane] = rp.word | nw;  // the other words keep their bits
+    }
+    if (lane == 0 && p.counters && selected > 0)
+      atomicAdd(p.counters + WISE_CTR_SELECTED, static_cast<unsigned long long>(selected));
+    return;
+  }
   // the arrival goes out before the support stores, which overlap its round trip
   unsigned int *arrive = reinterpret_cast<unsigned int *>(&tag->reserved);
   unsigned int all = 0u;
@@ -728,8 +803,17 @@ __global__ __launch_bounds__(64 * W) void split_fused_kernel(const SplitParams p
   if (k < items)
     run_item<kBf16, D, kKOnly>(p, u, r, h, k, rp.n, sparse, count, word, incl, lane, s_tiles[k], T, &lds);
   __syncthreads();  // every wave of the workgroup reaches this once
-  if (k == 0) finish_output<D, kKOnly>(p, u, items, s_acc, s_ml, s_w, lane);
-  if (k == 1) finish_row<kKOnly, MAXB>(p, rp, u, h, nb, items, s_ml, s_st, s_bits, lane);
+  // short units of calls that read V: wave 0 carries the row's arrival
+  // (long units: measured 1% slower at 8K, where twice as many workgroups
+  // end with the selected-block counter atomics)
+  constexpr bool kEarlyArrival = !kKOnly && MAXB <= kMaxFusedBlocks;
+  if constexpr (kEarlyArrival) {
+    if (k == 0) finish_output_arrive<D>(p, rp, u, h, nb, items, s_acc, s_ml, s_w, lane);
+    if (k == 1) finish_row<kKOnly, MAXB, false>(p, rp, u, h, nb, items, s_ml, s_st, s_bits, lane);
+  } else {
+    if (k == 0) finish_output<D, kKOnly>(p, u, items, s_acc, s_ml, s_w, lane);
+    if (k == 1) finish_row<kKOnly, MAXB, true>(p, rp, u, h, nb, items, s_ml, s_st, s_bits, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
