@@ -135,3 +135,23 @@ def test_one_launch_decode_completes_the_call(torch, ctx, rows):
         harness.call(dev, ws, W.WISE_DENSE)
         torch.cuda.synchronize()
         assert torch.equal(d_only, dev.out), "dense decode alone differs"
+
+
+def test_split_grid_calls_need_the_finish(torch):
+    """Where wise_fused_waves() is 0 (contexts beyond 8K) the decode call only
+    leaves partials in the workspace: the output stays untouched until
+    wise_finish_select merges them."""
+    w = dataclasses.replace(synth.WORKLOADS["ctx1k"], rows=2, ctx=9000, name="split_grid")
+    assert W.wise_fused_waves(w.rows, w.heads, w.head_dim, w.max_ctx, W.WISE_BF16, True) == 0
+    ws = harness.Workspace(w.rows, w.heads, w.head_dim, w.max_ctx)
+    dev = harness.upload(synth.layer_inputs(w, 0))
+    st = harness.SupportState(w.rows, w.heads, w.max_ctx)
+    dev.out.fill_(float("nan"))
+    harness.call(dev, ws, W.WISE_DISCOVER, st, required=1, finish=False)
+    torch.cuda.synchronize()
+    assert torch.isnan(dev.out).all(), "the decode call wrote the output"
+    assert int(st.counters[W.CTR_SELECTED]) == 0 and int(st.support.abs().sum()) == 0
+    harness.call(dev, ws, W.WISE_DISCOVER, st, required=1)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dev.out).any()
+    assert int(st.counters[W.CTR_SELECTED]) > 0
